@@ -1,0 +1,315 @@
+"""Benchmark of the MoE token-routing data path on one MI355X.
+
+One step = one pass of the whole path over one routed batch: (routing-map
+compaction, for the compaction workload) -> route_prep -> gather (binned or
+padded) -> weighted scatter-combine -> wgrad, with every buffer preallocated
+and every call going through the C ABI of libpeg.so on torch's current
+stream. Steps rotate over several copies of the input (distinct buffers) so
+that the bytes of a step are not served from the 256 MB Infinity Cache left
+warm by the previous step.
+
+Printed: one JSON line. ``value`` is the effective HBM bandwidth of the step,
+(algorithmic bytes of gather + combine + wgrad) / (wall time of the step,
+route_prep and compaction included); ``roofline`` is the dominant kernel's
+algorithmic bytes / its average duration (HIP events on its stream);
+``cpu_baseline`` is the CPU oracle on the same workload.
+
+Algorithmic bytes per launch (s = element bytes, U = tokens with a kept
+route, N = kept assignments, R = expert-tensor rows):
+  gather  = U*H*s + R*H*s + 4*T*K + 8*E
+  combine = N*H*s + T*H*s + 8*T*K
+  wgrad   = N*H*s + U*H*s + 8*T*K
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0  # MI355X HBM3E
+WORKLOADS = {1: "configs[0]", 2: "configs[1]"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "padded_expert_gather_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, help="workload id 1-5 (default 2: Mixtral-8x7B-shaped)")
+    ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: enough for 2 GiB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
+    ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
+    return ap.parse_args()
+
+
+class Step:
+    """Preallocated buffers and precomputed C-ABI arguments of one input copy."""
+
+    def __init__(self, peg, torch, wl, dev, host):
+        import workloads as W
+        self.W = W
+        lib = peg.library()
+        self.lib = lib
+        T, H, E, K = wl.T, wl.H, wl.E, wl.K
+        self.wl = wl
+        i32 = dict(dtype=torch.int32, device=dev)
+        tdt = {W.F32: torch.float32, W.BF16: torch.bfloat16, W.F16: torch.float16}[wl.dtype]
+        self.x = host["x"].to(dev)
+        self.grad = host["grad"].to(dev)
+        if wl.routing_map is not None:
+            self.probs = host["probs"].to(dev)
+            self.rmap = host["rmap"].to(dev)
+            self.top = torch.empty((T, K), **i32)
+            self.w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        else:
+            self.top = host["top"].to(dev)
+            self.w = host["w"].to(dev)
+        total = T * K
+        self.indices = torch.empty(total, **i32)
+        self.bin_ids = torch.empty(total, **i32)
+        self.tpe = torch.empty(E, **i32)
+        self.bins = torch.empty(E, **i32)
+        self.padded_bins = torch.empty(E, **i32) if wl.layout == W.PADDED else None
+        self.slot_row = torch.empty(total, **i32)
+        self.ws = torch.empty(peg.workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)
+        self.R = host["R"]
+        self.y = torch.empty((self.R, H), dtype=tdt, device=dev)
+        self.out = torch.empty((T, H), dtype=tdt, device=dev)
+        self.wg = torch.empty((T, K), dtype=torch.float32, device=dev)
+        P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        wsb = self.ws.numel()
+        cap = wl.capacity or 0
+        m = wl.pad_multiple or 0
+        self.calls = {}
+        if wl.routing_map is not None:
+            self.calls["compact"] = (lib.peg_routing_map_compact,
+                                     (P(self.probs), 0, P(self.rmap), T, E, wl.topk, P(self.w), P(self.top), st))
+        self.calls["route_prep"] = (lib.peg_route_prep,
+                                    (P(self.top), T, K, E, wl.layout, cap, m, P(self.indices), P(self.bin_ids),
+                                     P(self.tpe), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.ws),
+                                     wsb, st))
+        if wl.layout == W.BINNED:
+            self.calls["gather"] = (lib.peg_gather_binned,
+                                    (P(self.x), wl.dtype, T, H, K, E, cap, P(self.indices), P(self.bin_ids),
+                                     P(self.bins), P(self.slot_row), P(self.y), P(self.ws), wsb, st))
+        else:
+            self.calls["gather"] = (lib.peg_gather_padded,
+                                    (P(self.x), wl.dtype, T, H, K, E, P(self.indices), P(self.bin_ids), P(self.bins),
+                                     P(self.padded_bins), P(self.slot_row), P(self.y), self.R, None, P(self.ws), wsb,
+                                     st))
+        self.calls["combine"] = (lib.peg_scatter_combine,
+                                 (P(self.y), wl.dtype, wl.layout, T, H, K, E, cap, P(self.indices), P(self.bin_ids),
+                                  P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.w), P(self.out),
+                                  P(self.ws), wsb, st))
+        self.calls["wgrad"] = (lib.peg_wgrad,
+                               (P(self.y), P(self.grad), wl.dtype, wl.layout, T, H, K, E, cap, P(self.indices),
+                                P(self.bin_ids), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.wg),
+                                P(self.ws), wsb, st))
+        self.order = list(self.calls)
+
+    def run(self, events=None):
+        for i, name in enumerate(self.order):
+            fn, args = self.calls[name]
+            if events is not None:
+                events[name][0].record()
+            rc = fn(*args)
+            if rc != 0:
+                raise RuntimeError(f"{name} failed with status {rc}")
+            if events is not None:
+                events[name][1].record()
+
+
+def host_inputs(torch, W, wl, peg, dev):
+    """Host tensors of a workload and its expert-tensor row count."""
+    def t16(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16 if wl.dtype == W.BF16 else torch.float16)
+    conv = (lambda a: torch.from_numpy(a)) if wl.dtype == W.F32 else t16
+    host = {"x": conv(wl.x), "grad": conv(wl.grad)}
+    if wl.routing_map is not None:
+        host["probs"] = torch.from_numpy(wl.probs)
+        host["rmap"] = torch.from_numpy(wl.routing_map)
+        pg, ig = peg.routing_map_compact(host["probs"].to(dev), host["rmap"].to(dev), wl.topk)
+        top_dev = ig
+    else:
+        host["top"] = torch.from_numpy(wl.top_experts)
+        host["w"] = torch.from_numpy(wl.weights)
+        top_dev = host["top"].to(dev)
+    if wl.layout == W.BINNED:
+        r = peg.route_prep(top_dev, wl.E, capacity=wl.capacity)
+        R = wl.E * wl.capacity
+    else:
+        r = peg.route_prep(top_dev, wl.E, pad_multiple=wl.pad_multiple)
+        R = r.expert_rows()
+    host["R"] = R
+    # sizes for the algorithmic byte counts, from the device routing
+    kept = (r.slot_row >= 0).reshape(wl.T, wl.K)
+    N = int(kept.sum().item())
+    U = int(kept.any(dim=1).sum().item())
+    return host, dict(R=R, N=N, U=U, n=r.num_valid())
+
+
+def algorithmic_bytes(wl, sz, s):
+    T, H, E, K = wl.T, wl.H, wl.E, wl.K
+    return {
+        "gather": sz["U"] * H * s + sz["R"] * H * s + 4 * T * K + 8 * E,
+        "combine": sz["N"] * H * s + T * H * s + 8 * T * K,
+        "wgrad": sz["N"] * H * s + sz["U"] * H * s + 8 * T * K,
+    }
+
+
+def cpu_baseline(wl, W, seconds, bytes_step):
+    """The CPU oracle, as it stands, on the same workload: whole steps
+    (compaction, route_prep, gather, combine, wgrad) repeated until about
+    ``seconds`` of CPU time; single-threaded scalar C."""
+    import oracle
+    reps, t_total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        if wl.routing_map is not None:
+            w, top = oracle.routing_map_compact(wl.probs, W.F32, wl.routing_map, wl.topk)
+        else:
+            w, top = wl.weights, wl.top_experts
+        m = wl.pad_multiple if wl.layout == W.PADDED else None
+        cap = wl.capacity if wl.layout == W.BINNED else None
+        r = oracle.route_prep(top, wl.E, pad_multiple=m)
+        y = oracle.gather(wl.x, r, wl.layout, cap)
+        oracle.scatter_combine(y, wl.dtype, r, wl.layout, cap, weights=w.reshape(-1))
+        oracle.wgrad(y, wl.grad, wl.dtype, r, wl.layout, cap)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if t_total >= seconds or reps >= 50:
+            break
+    per_step = t_total / reps
+    return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole step(s) of the same workload (seed 0), {per_step * 1e3:.1f} ms per step, "
+                      f"1 thread; tokens/s {wl.T / per_step:.1f}"}
+
+
+def traffic_for(kernel, workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(workload_name, {}).get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the data path is a "
+              f"single-GPU library; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np  # noqa: F401
+    import torch
+    import padded_expert_gather_amd as peg
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating workload {args.workload}")
+    wl = W.config(args.workload, 0)
+    host, sz = host_inputs(torch, W, wl, peg, dev)
+    s = 4 if wl.dtype == W.F32 else 2
+    ab = algorithmic_bytes(wl, sz, s)
+    bytes_step = sum(ab.values())
+    per_set = (wl.T * wl.H * s) * 3 + sz["R"] * wl.H * s
+    sets = args.sets or max(2, min(16, math.ceil(2 * 2 ** 30 / per_set)))
+    log(f"R={sz['R']} N={sz['N']} U={sz['U']} step bytes={bytes_step / 1e6:.1f} MB, {sets} input copies")
+    steps_obj = [Step(peg, torch, wl, dev, host) for _ in range(sets)]
+    torch.cuda.synchronize()
+
+    names = steps_obj[0].order
+    for i in range(args.warmup):
+        steps_obj[i % sets].run()
+    torch.cuda.synchronize()
+
+    use_ev = not args.no_events
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)] if use_ev else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        steps_obj[(args.warmup + i) % sets].run(evs[i] if use_ev else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = bytes_step / (ms_step / 1e3) / 1e9
+
+    kernels = {}
+    if use_ev:
+        for n in names:
+            ms = [evs[i][n][0].elapsed_time(evs[i][n][1]) for i in range(args.steps)]
+            avg = sum(ms) / len(ms)
+            entry = {"avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2)}
+            if n in ab:
+                entry["bytes"] = ab[n]
+                entry["GBps"] = round(ab[n] / (avg / 1e3) / 1e9, 1)
+                entry["frac_peak"] = round(ab[n] / (avg / 1e3) / 1e9 / PEAK_GBS, 4)
+            kernels[n] = entry
+    dominant = max(ab, key=lambda n: kernels[n]["avg_us"]) if use_ev else None
+    roofline = None
+    if dominant:
+        achieved = kernels[dominant]["GBps"]
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic_for(dominant, wl.name),
+                    "bytes_per_launch": ab[dominant], "avg_us": kernels[dominant]["avg_us"]}
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(wl, W, args.cpu_seconds, bytes_step)
+
+    dtype_name = W.DTYPE_NAMES[wl.dtype]
+    line = {
+        "metric": "effective HBM GB/s (and % of peak) for gather+scatter+wgrad; routed tokens/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype_name, "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K,
+                   "layout": "binned" if wl.layout == W.BINNED else "padded",
+                   "capacity": wl.capacity or None, "pad_multiple": wl.pad_multiple or None,
+                   "compaction": wl.routing_map is not None, "input_copies": sets,
+                   "rows": sz["R"], "kept": sz["N"], "tokens_with_route": sz["U"]},
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "routed_tokens_per_s": round(wl.T / (ms_step / 1e3), 1),
+        "step_bytes": bytes_step,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+// gather.hip - dispatch of token rows into the expert tensor (binned
+// [E, C, H] or padded [padded_bins[E-1], H]) on gfx950.
+//
+// What is computed ("Build Triton-Ascend Binned MoE Routing": Goal, Workflow
+// step 3, Implementation Pattern, Ascend Guardrails; "Build Triton-Ascend
+// Padded MoE Routing": Workflow steps 4-5, Implementation Pattern, Ascend
+// Guardrails): every kept sorted position copies token indices[i] / TOP_K
+// into its row; every other row of the tensor is zero.
+//
+// How (MI355X design, not the pages' Ascend sub-block buffering):
+//   * token-major: one block per token reads the token row once from HBM
+//     into VGPRs (16-byte lanes) and stores it to each of its <= K rows, so
+//     the source is read exactly once however many experts it goes to;
+//   * the rows of a token come from the assignment -> row map (slot_row)
+//     staged in LDS;
+//   * in the same launch, trailing "gap" blocks write zeros into the unused
+//     capacity / padding rows only (each gap of an expert is one contiguous
+//     byte range), so no row is written twice and no memset pass is needed.
+#include "peg_device.hpp"
+#include "peg_host.hpp"
+
+namespace peg {
+
+constexpr int kGatherUnroll = 4;
+
+template <int VEC>
+__global__ __launch_bounds__(kBlock) void gather_kernel(
+    const uint8_t* __restrict__ x, uint8_t* __restrict__ out, int64_t nch, int32_t K,
+    const int32_t* __restrict__ slot_row, int64_t out_rows, int32_t layout, int32_t E, int32_t capacity,
+    const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int64_t token_blocks,
+    uint32_t* __restrict__ err_flag) {
+    using V = typename VecOf<VEC>::T;
+    const int64_t row_bytes = nch * VEC;
+
+    if ((int64_t)blockIdx.x < token_blocks) {
+        // ---------------- token rows -> their expert rows ----------------
+        __shared__ int srow[PEG_MAX_EXPERTS];
+        __shared__ int s_nv;
+        const int64_t t = blockIdx.x;
+        bool overflow = false;
+        for (int k = threadIdx.x; k < K; k += kBlock) {
+            int r = slot_row[t * K + k];
+            if (r >= out_rows) {
+                overflow = true;
+                r = -1;
+            }
+            srow[k] = r;
+        }
+        if (overflow && err_flag) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
+        __syncthreads();
+        if (threadIdx.x == 0) {  // keep the valid rows, in k order
+            int nv = 0;
+            for (int k = 0; k < K; ++k) {
+                int r = srow[k];
+                if (r >= 0) srow[nv++] = r;
+            }
+            s_nv = nv;
+        }
+        __syncthreads();
+        const int nv = s_nv;
+        if (nv == 0) return;  // token fully dropped: its row is never read
+        const uint8_t* src = x + t * row_bytes;
+        for (int64_t c0 = threadIdx.x; c0 < nch; c0 += (int64_t)kBlock * kGatherUnroll) {
+            V v[kGatherUnroll];
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const int64_t c = c0 + (int64_t)u * kBlock;
+                if (c < nch) v[u] = load_vec<VEC>(src, c);
+            }
+            for (int j = 0; j < nv; ++j) {
+                uint8_t* dst = out + (int64_t)srow[j] * row_bytes;
+#pragma unroll
+                for (int u = 0; u < kGatherUnroll; ++u) {
+                    const int64_t c = c0 + (int64_t)u * kBlock;
+                    if (c < nch) store_vec<VEC>(dst, c, v[u]);
+                }
+            }
+        }
+        return;
+    }
+
+    // ---------------- zero the gap rows ----------------
+    // gap of expert e = rows [gstart[e], gstart[e] + glen[e]); gpre = exclusive
+    // prefix of glen. Rows at or past out_rows are never touched.
+    __shared__ int gpre[PEG_MAX_EXPERTS + 1];
+    __shared__ int gstart[PEG_MAX_EXPERTS];
+    __shared__ int scratch[kBlock / kWave];
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kBlock) {
+        const int e = e0 + threadIdx.x;
+        int len = 0, start = 0;
+        if (e < E) {
+            int count = bins[e] - (e ? bins[e - 1] : 0);
+            count = count < 0 ? 0 : count;
+            int64_t s, g;
+            if (layout == PEG_BINNED) {
+                const int kept = count < capacity ? count : capacity;
+                s = (int64_t)e * capacity + kept;
+                g = capacity - kept;
+            } else {
+                const int64_t ps = e ? padded_bins[e - 1] : 0;
+                s = ps + count;
+                g = (int64_t)padded_bins[e] - s;
+            }
+            if (g <= 0 || s < 0 || s >= out_rows) g = 0;   // no gap, or it starts past the buffer
+            else if (s + g > out_rows) g = out_rows - s;   // gap cut at the end of the buffer
+            len = (int)g;
+            start = (int)(g > 0 ? s : 0);
+        }
+        int total;
+        int pre = block_exclusive_scan<kBlock>(len, scratch, &total);
+        if (e < E) {
+            gpre[e] = carry + pre;
+            gstart[e] = start;
+        }
+        carry += total;
+    }
+    if (threadIdx.x == 0) gpre[E] = carry;
+    __syncthreads();
+
+    const int64_t units = (int64_t)carry * nch;
+    const int64_t nz = (int64_t)gridDim.x - token_blocks;
+    const int64_t zb = (int64_t)blockIdx.x - token_blocks;
+    const int64_t lo = units * zb / nz;
+    const int64_t hi = units * (zb + 1) / nz;
+    int64_t u = lo + threadIdx.x;
+    if (u >= hi) return;
+    // expert holding unit u: last e with gpre[e] * nch <= u
+    int a = 0, b = E - 1;
+    while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if ((int64_t)gpre[mid] * nch <= u) a = mid;
+        else b = mid - 1;
+    }
+    int e = a;
+    const V z = zero_vec<VEC>();
+    for (; u < hi; u += kBlock) {
+        while ((int64_t)gpre[e + 1] * nch <= u) ++e;
+        const int64_t dst_unit = (int64_t)gstart[e] * nch + (u - (int64_t)gpre[e] * nch);
+        store_vec<VEC>(out, dst_unit, z);
+    }
+}
+
+// Zero-fill blocks: enough that each writes a few hundred KB at most.
+static int64_t gap_blocks(int64_t max_gap_rows, int64_t nch, int vec) {
+    const int64_t units = max_gap_rows * nch;
+    int64_t b = (units + 4096 - 1) / 4096;
+    (void)vec;
+    if (b < 1) b = 1;
+    if (b > 2048) b = 2048;
+    return b;
+}
+
+static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
+                                int32_t layout, int32_t capacity, const int32_t* indices, const int32_t* bin_ids,
+                                const int32_t* bins, const int32_t* padded_bins, const int32_t* slot_row,
+                                void* out, int64_t out_rows, uint32_t* err_flag, void* ws, size_t ws_bytes,
+                                void* stream) {
+    if (!dtype_ok(dtype)) return PEG_ERR_BAD_DTYPE;
+    if (T < 0 || H < 1 || K < 1 || E < 1 || E > PEG_MAX_EXPERTS) return PEG_ERR_BAD_SHAPE;
+    if (K > PEG_MAX_EXPERTS || T > kMaxAssign / K || out_rows < 0 || out_rows > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(dtype);
+    if (H > (int64_t(1) << 40) / eb) return PEG_ERR_BAD_SHAPE;
+    if ((!x && T > 0) || (!out && out_rows > 0) || !bins || (layout == PEG_PADDED && !padded_bins))
+        return PEG_ERR_NULL_ARG;
+    if (!slot_row && T > 0 && (!indices || !bin_ids)) return PEG_ERR_NULL_ARG;
+    const int64_t row_bytes = H * eb;
+    if (!aligned(x, eb) || !aligned(out, eb)) return PEG_ERR_ALIGNMENT;
+    const int vec = pick_vec(row_bytes, eb, x, out);
+    if (vec == 0) return PEG_ERR_ALIGNMENT;
+    const int64_t total = T * (int64_t)K;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!slot_row) {
+        if (!ws) return PEG_ERR_WORKSPACE;
+        if (ws_bytes < ws_need(T, K, E)) return PEG_ERR_WORKSPACE;
+        int32_t* rebuilt = reinterpret_cast<int32_t*>(ws);
+        PEG_CHECK(rebuild_slot_row(total, E, layout, capacity, indices, bin_ids, bins, padded_bins, rebuilt, s));
+        slot_row = rebuilt;
+    }
+    const int64_t nch = row_bytes / vec;
+    const int64_t nz = gap_blocks(out_rows, nch, vec);
+    const dim3 grid((unsigned)(T + nz));
+    switch (vec) {
+        case 16:
+            return launch(gather_kernel<16>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
+                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
+        case 8:
+            return launch(gather_kernel<8>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
+                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
+        case 4:
+            return launch(gather_kernel<4>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
+                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
+        default:
+            return launch(gather_kernel<2>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
+                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
+    }
+}
+
+}  // namespace peg
+
+using namespace peg;
+
+PEG_API peg_status peg_gather_binned(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
+                                     int32_t capacity, const int32_t* indices, const int32_t* bin_ids,
+                                     const int32_t* bins, const int32_t* slot_row, void* out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    if (capacity < 1 || E < 1 || (int64_t)E * capacity > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    return gather_common(x, dtype, T, H, K, E, PEG_BINNED, capacity, indices, bin_ids, bins, nullptr, slot_row,
+                         out, (int64_t)E * capacity, nullptr, ws, ws_bytes, stream);
+}
+
+PEG_API peg_status peg_gather_padded(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
+                                     const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
+                                     const int32_t* padded_bins, const int32_t* slot_row, void* out,
+                                     int64_t out_rows, uint32_t* err_flag, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    return gather_common(x, dtype, T, H, K, E, PEG_PADDED, 0, indices, bin_ids, bins, padded_bins, slot_row, out,
+                         out_rows, err_flag, ws, ws_bytes, stream);
+}

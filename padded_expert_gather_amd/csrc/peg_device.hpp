@@ -1,0 +1,191 @@
+// peg_device.hpp - device-side building blocks of the gfx950 kernels:
+// element codecs, 16/8/4/2-byte row vectors, wave64 scans and reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "peg.h"
+
+namespace peg {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A row is moved as VEC-byte lanes: 16 (dwordx4), 8, 4 or 2 bytes.
+template <int VEC> struct VecOf;
+template <> struct VecOf<16> { using T = u32x4; };
+template <> struct VecOf<8> { using T = u32x2; };
+template <> struct VecOf<4> { using T = uint32_t; };
+template <> struct VecOf<2> { using T = uint16_t; };
+
+template <int VEC>
+__device__ __forceinline__ typename VecOf<VEC>::T load_vec(const uint8_t* base, int64_t unit) {
+    return reinterpret_cast<const typename VecOf<VEC>::T*>(base)[unit];
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_vec(uint8_t* base, int64_t unit, typename VecOf<VEC>::T v) {
+    reinterpret_cast<typename VecOf<VEC>::T*>(base)[unit] = v;
+}
+
+template <int VEC>
+__device__ __forceinline__ typename VecOf<VEC>::T zero_vec() {
+    return typename VecOf<VEC>::T(0);
+}
+
+// ---------------------------------------------------------------------------
+// Element codecs. Widening is exact; narrowing rounds to nearest even.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h16) {
+    return __uint_as_float(h16 << 16);
+}
+
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // NaN stays a quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                 // ties to even
+    return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h16) {
+    uint16_t b = (uint16_t)h16;
+    _Float16 h;
+    __builtin_memcpy(&h, &b, 2);
+    return (float)h;
+}
+
+__device__ __forceinline__ uint32_t float_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;  // hardware conversion, round to nearest even
+    uint16_t b;
+    __builtin_memcpy(&b, &h, 2);
+    return b;
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<PEG_F32> {
+    static constexpr int bytes = 4;
+};
+template <> struct Elem<PEG_BF16> {
+    static constexpr int bytes = 2;
+};
+template <> struct Elem<PEG_F16> {
+    static constexpr int bytes = 2;
+};
+
+template <int DT>
+__device__ __forceinline__ float decode(uint32_t bits) {
+    if constexpr (DT == PEG_F32) return __uint_as_float(bits);
+    else if constexpr (DT == PEG_BF16) return bf16_bits_to_float(bits);
+    else return f16_bits_to_float(bits);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t encode(float v) {
+    if constexpr (DT == PEG_F32) return __float_as_uint(v);
+    else if constexpr (DT == PEG_BF16) return float_to_bf16_bits(v);
+    else return float_to_f16_bits(v);
+}
+
+// Unpack a VEC-byte vector into its N = VEC / element-bytes elements (as
+// float), and pack them back.
+template <int DT, int VEC>
+struct Lanes {
+    static constexpr int EB = Elem<DT>::bytes;
+    static constexpr int N = VEC / EB;
+    using V = typename VecOf<VEC>::T;
+
+    __device__ static __forceinline__ void unpack(const V& v, float (&f)[N]) {
+        if constexpr (VEC == 2) {
+            f[0] = decode<DT>((uint32_t)v);
+        } else {
+            constexpr int W = VEC / 4;
+            uint32_t w[W];
+            __builtin_memcpy(w, &v, VEC);
+            if constexpr (EB == 4) {
+#pragma unroll
+                for (int i = 0; i < W; ++i) f[i] = decode<DT>(w[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < W; ++i) {
+                    f[2 * i] = decode<DT>(w[i] & 0xffffu);
+                    f[2 * i + 1] = decode<DT>(w[i] >> 16);
+                }
+            }
+        }
+    }
+
+    __device__ static __forceinline__ V pack(const float (&f)[N]) {
+        V v;
+        if constexpr (VEC == 2) {
+            v = (uint16_t)encode<DT>(f[0]);
+        } else {
+            constexpr int W = VEC / 4;
+            uint32_t w[W];
+            if constexpr (EB == 4) {
+#pragma unroll
+                for (int i = 0; i < W; ++i) w[i] = encode<DT>(f[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < W; ++i) w[i] = encode<DT>(f[2 * i]) | (encode<DT>(f[2 * i + 1]) << 16);
+            }
+            __builtin_memcpy(&v, w, VEC);
+        }
+        return v;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Wave64 / block primitives.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t lanes_below() {
+    return (uint64_t(1) << lane_id()) - 1;  // lane 0 -> 0
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int y = __shfl_up(v, d, kWave);
+        if (lane >= d) v += y;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the NT threads of a block (NT a multiple of 64).
+// `scratch` holds NT/64 ints of LDS. Returns the prefix of this thread's
+// value; *total receives the block-wide sum. Contains barriers: every
+// thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id();
+    const int w = threadIdx.x / kWave;
+    int inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < NW ? scratch[lane] : 0;
+        t = wave_inclusive_scan(t);
+        if (lane < NW) scratch[lane] = t;
+    }
+    __syncthreads();
+    int prefix = (w ? scratch[w - 1] : 0) + inc - v;
+    *total = scratch[NW - 1];
+    __syncthreads();
+    return prefix;
+}
+
+}  // namespace peg

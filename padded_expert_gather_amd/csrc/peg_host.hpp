@@ -1,0 +1,89 @@
+// peg_host.hpp - host-side helpers shared by the launchers: argument checks,
+// launch wrapper, row-vector width choice, workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "peg.h"
+
+#define PEG_API extern "C" __attribute__((visibility("default")))
+
+namespace peg {
+
+constexpr int kBlock = 256;        // threads per block of the streaming kernels
+constexpr int64_t kMaxAssign = (int64_t(1) << 31) - 1;
+
+inline bool dtype_ok(int32_t dt) { return dt == PEG_F32 || dt == PEG_BF16 || dt == PEG_F16; }
+inline int elem_bytes(int32_t dt) { return dt == PEG_F32 ? 4 : 2; }
+inline bool layout_ok(int32_t l) { return l == PEG_BINNED || l == PEG_PADDED; }
+
+inline bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+// Largest lane width in {16, 8, 4, 2} that divides the row length in bytes
+// and the address of every row buffer; 0 if even the element size fails.
+inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, const void* c = nullptr) {
+    for (int v = 16; v >= eb; v >>= 1) {
+        if (row_bytes % v) continue;
+        if (!aligned(a, v) || !aligned(b, v) || (c && !aligned(c, v))) continue;
+        return v;
+    }
+    return 0;
+}
+
+// Tiles of the routing preparation: 256 threads x ITEMS assignments. The
+// per-chunk count table of a tile (4 * ITEMS chunks of 64 x E ints) stays
+// within 32 KB of LDS.
+inline int prep_items(int32_t E) { return E <= 256 ? 8 : (E <= 512 ? 4 : 2); }
+inline int64_t prep_tile(int32_t E) { return (int64_t)kBlock * prep_items(E); }
+inline int64_t prep_tiles(int64_t total, int32_t E) { return (total + prep_tile(E) - 1) / prep_tile(E); }
+
+// Workspace: every call uses one region starting at offset 0.
+inline size_t ws_need(int64_t T, int32_t K, int32_t E) {
+    int64_t total = T * (int64_t)K;
+    size_t tile_counts = (size_t)prep_tiles(total, E) * (size_t)E * 4;  // route_prep
+    size_t slots = (size_t)total * 4;                                   // slot_row rebuild
+    size_t bitmap = (size_t)((total + 31) / 32) * 4 + 64;               // validation
+    size_t need = tile_counts;
+    if (slots > need) need = slots;
+    if (bitmap > need) need = bitmap;
+    need = (need + 255) & ~size_t(255);
+    return need < 256 ? 256 : need;
+}
+
+// Launch through hipLaunchKernel so that the status of this very launch is
+// returned (no reliance on the thread's sticky last-error state).
+template <typename... KArgs, size_t... I>
+inline void fill_argv(std::tuple<KArgs...>& t, void** argv, std::index_sequence<I...>) {
+    ((argv[I] = (void*)&std::get<I>(t)), ...);
+}
+
+template <typename... KArgs, typename... Args>
+inline peg_status launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                         Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    if (grid.x == 0 || grid.y == 0 || grid.z == 0) return PEG_OK;
+    std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+    void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    fill_argv(vals, argv, std::index_sequence_for<KArgs...>{});
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, s);
+    return e == hipSuccess ? PEG_OK : PEG_ERR_LAUNCH;
+}
+
+// Rebuilds the assignment -> row map from the sorted routing arrays into the
+// workspace (internal; shared by the gathers, the combine and wgrad).
+peg_status rebuild_slot_row(int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                            const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
+                            const int32_t* padded_bins, int32_t* slot_row, hipStream_t s);
+
+}  // namespace peg
+
+#define PEG_CHECK(x)                        \
+    do {                                    \
+        peg_status st_ = (x);               \
+        if (st_ != PEG_OK) return st_;      \
+    } while (0)
