@@ -17,7 +17,8 @@ from ctypes import c_int32, c_int64, c_size_t, c_void_p
 import torch  # loads torch's HIP runtime first; libpeg then binds to the same one
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpeg.so")
+# PEG_LIBRARY may name another build of the same sources (a tuning variant)
+LIB_PATH = os.environ.get("PEG_LIBRARY") or os.path.join(HERE, "libpeg.so")
 
 F32, BF16, F16 = 0, 1, 2
 BINNED, PADDED = 0, 1

@@ -33,30 +33,33 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src):
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src, objdir, extra):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose=False):
-    """Compile every HIP source (always) and link libpeg.so. Returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose=False, extra_flags=(), out=LIB):
+    """Compile every HIP source (always) and link the library (default
+    libpeg.so). ``extra_flags`` may set the tuning macros (-DPEG_...) for a
+    variant build written to ``out``. Returns the library path."""
+    objdir = OBJDIR if out == LIB else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, objdir, list(extra_flags)), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(LIB)
-    return LIB
+        print(out)
+    return out
 
 
 def is_stale():

@@ -10,170 +10,212 @@
 //   wgrad: wgrad[a] = <y[row(a)], grad[a / K]> for kept a, else 0 (Workflow
 //     step 6 of both pages; fp32 accumulation per their Ascend Guardrails).
 //
-// How: token-major. One block per token stages the token's kept rows (and
-// weights) in LDS, then streams its H columns in 16-byte lanes: every kept
-// expert row is read once, the output row (combine) is written once, the
-// gradient row (wgrad) is read once for all K dots. Accumulation is fp32
-// FMA; the wgrad dots finish with a wave64 butterfly and a 4-wave LDS sum.
-// Rows that are unused capacity, padding or dropped are never read.
+// How: token-major. One block per token; the token's rows (and weights) come
+// in by wave-uniform scalar loads, and each of the 4 waves streams its
+// quarter of the H columns in 16-byte lanes: every kept expert row is read
+// once, the output row (combine) is written once, the gradient row (wgrad)
+// is read once for all K dots. Accumulation is fp32 FMA; the wgrad dots
+// finish with a wave64 butterfly and a 4-wave sum in LDS. Rows that are
+// unused capacity, padding or dropped are never read.
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
 namespace peg {
 
-constexpr int kCombUnroll = 2;  // column vectors per thread per pass
-constexpr int kKBatch = 4;      // expert rows loaded together before use
-
-// Stage the kept (row, weight, k) of token t in LDS, in k order. Returns the
-// number kept. Rows outside [0, R) are treated as not kept.
-__device__ __forceinline__ int stage_token(int64_t t, int32_t K, const int32_t* __restrict__ slot_row,
-                                           const float* __restrict__ weights, int64_t R, int* srow, float* sw,
-                                           int* sk, int* s_nv) {
-    for (int k = threadIdx.x; k < K; k += kBlock) {
-        int r = slot_row[t * K + k];
-        if (r < 0 || r >= R) r = -1;
-        srow[k] = r;
-        if (sw) sw[k] = weights ? weights[t * K + k] : 1.0f;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int nv = 0;
-        for (int k = 0; k < K; ++k) {
-            const int r = srow[k];
-            if (r >= 0) {
-                srow[nv] = r;
-                if (sw) sw[nv] = sw[k];
-                if (sk) sk[nv] = k;
-                ++nv;
-            }
-        }
-        *s_nv = nv;
-    }
-    __syncthreads();
-    return *s_nv;
-}
+#ifndef PEG_KBATCH
+#define PEG_KBATCH 4
+#endif
+constexpr int kKBatch = PEG_KBATCH;  // expert rows loaded together before they are used
 
 __device__ __forceinline__ int64_t expert_rows(int64_t static_rows, const int32_t* padded_bins, int32_t E) {
     return padded_bins ? (int64_t)padded_bins[E - 1] : static_rows;
 }
 
-template <int DT, int VEC>
+// Row of route k of a token, -1 when the route is absent, dropped or outside
+// [0, R). Wave-uniform (scalar) loads.
+__device__ __forceinline__ int route_row(const int32_t* __restrict__ rows, int k, int K, int64_t R) {
+    if (k >= K) return -1;
+    const int r = rows[k];
+    return (r < 0 || r >= R) ? -1 : r;
+}
+
+// Columns of a token row are split into 4 contiguous quarters, one per wave
+// of the block; a wave covers its quarter in passes of 64 lanes x U vectors.
+template <int DT, int VEC, int U>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restrict__ y, uint8_t* __restrict__ out,
-                                                         int64_t nch, int32_t K, const int32_t* __restrict__ slot_row,
+                                                         int64_t nch, int64_t quarter, int32_t K,
+                                                         const int32_t* __restrict__ slot_row,
                                                          const float* __restrict__ weights, int64_t static_rows,
                                                          const int32_t* __restrict__ padded_bins, int32_t E) {
     using L = Lanes<DT, VEC>;
     using V = typename L::V;
     constexpr int N = L::N;
-    __shared__ int srow[PEG_MAX_EXPERTS];
-    __shared__ float sw[PEG_MAX_EXPERTS];
-    __shared__ int s_nv;
     const int64_t t = blockIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    const int64_t c_begin = w * quarter;
+    const int64_t c_end = c_begin + quarter < nch ? c_begin + quarter : nch;
     const int64_t R = expert_rows(static_rows, padded_bins, E);
-    const int nv = stage_token(t, K, slot_row, weights, R, srow, sw, nullptr, &s_nv);
+    const int32_t* my_rows = slot_row + t * K;
+    const float* my_w = weights ? weights + t * K : nullptr;
+    int r8[kRowsFast];
+    float w8[kRowsFast];
+#pragma unroll
+    for (int k = 0; k < kRowsFast; ++k) {
+        r8[k] = route_row(my_rows, k, K, R);
+        w8[k] = (my_w && k < K) ? my_w[k] : 1.0f;
+    }
     const int64_t row_bytes = nch * VEC;
     uint8_t* dst = out + t * row_bytes;
 
-    for (int64_t c0 = threadIdx.x; c0 < nch; c0 += (int64_t)kBlock * kCombUnroll) {
-        float acc[kCombUnroll][N];
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
+        float acc[U][N];
 #pragma unroll
-        for (int u = 0; u < kCombUnroll; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < N; ++i) acc[u][i] = 0.0f;
-        for (int k0 = 0; k0 < nv; k0 += kKBatch) {
-            V v[kKBatch][kCombUnroll];
+#pragma unroll
+        for (int kb = 0; kb < kRowsFast; kb += kKBatch) {
+            V v[kKBatch][U];
 #pragma unroll
             for (int kk = 0; kk < kKBatch; ++kk) {
-                if (k0 + kk < nv) {
-                    const uint8_t* src = y + (int64_t)srow[k0 + kk] * row_bytes;
+                const int r = r8[kb + kk];
+                if (r < 0) continue;
+                const uint8_t* src = y + (int64_t)r * row_bytes;
 #pragma unroll
-                    for (int u = 0; u < kCombUnroll; ++u) {
-                        const int64_t c = c0 + (int64_t)u * kBlock;
-                        if (c < nch) v[kk][u] = load_vec<VEC>(src, c);
-                    }
+                for (int u = 0; u < U; ++u) {
+                    const int64_t c = c0 + u * kWave + lane;
+                    if (c < c_end) v[kk][u] = stream_load<VEC>(src, c);
                 }
             }
 #pragma unroll
             for (int kk = 0; kk < kKBatch; ++kk) {
-                if (k0 + kk < nv) {
-                    const float w = sw[k0 + kk];
+                if (r8[kb + kk] < 0) continue;
+                const float wk = w8[kb + kk];
 #pragma unroll
-                    for (int u = 0; u < kCombUnroll; ++u) {
-                        if (c0 + (int64_t)u * kBlock < nch) {
+                for (int u = 0; u < U; ++u) {
+                    if (c0 + u * kWave + lane < c_end) {
+                        float f[N];
+                        L::unpack(v[kk][u], f);
+#pragma unroll
+                        for (int i = 0; i < N; ++i) acc[u][i] = fmaf(wk, f[i], acc[u][i]);
+                    }
+                }
+            }
+        }
+        for (int k = kRowsFast; k < K; ++k) {  // routes beyond the first 8, one at a time
+            const int r = route_row(my_rows, k, K, R);
+            if (r < 0) continue;
+            const float wk = my_w ? my_w[k] : 1.0f;
+            const uint8_t* src = y + (int64_t)r * row_bytes;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u * kWave + lane;
+                if (c < c_end) {
+                    float f[N];
+                    L::unpack(stream_load<VEC>(src, c), f);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) acc[u][i] = fmaf(wk, f[i], acc[u][i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u * kWave + lane;
+            if (c < c_end) stream_store<VEC, PEG_NT_STORE_COMBINE>(dst, c, L::pack(acc[u]));
+        }
+    }
+}
+
+// wgrad: block per token, each wave dots its quarter of the columns for up
+// to 8 routes at a time; partial dots finish with a wave64 butterfly and a
+// 4-wave sum in LDS.
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
+                                                       float* __restrict__ wgrad, int64_t nch, int64_t quarter,
+                                                       int32_t K, const int32_t* __restrict__ slot_row,
+                                                       int64_t static_rows, const int32_t* __restrict__ padded_bins,
+                                                       int32_t E) {
+    using L = Lanes<DT, VEC>;
+    using V = typename L::V;
+    constexpr int N = L::N;
+    constexpr int NW = kBlock / kWave;
+    __shared__ float red[NW][kRowsFast];
+    const int64_t t = blockIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    const int64_t c_begin = w * quarter;
+    const int64_t c_end = c_begin + quarter < nch ? c_begin + quarter : nch;
+    const int64_t R = expert_rows(static_rows, padded_bins, E);
+    const int32_t* my_rows = slot_row + t * K;
+    const int64_t row_bytes = nch * VEC;
+    const uint8_t* g_row = grad + t * row_bytes;
+
+    for (int k0 = 0; k0 < K; k0 += kRowsFast) {
+        int r8[kRowsFast];
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < kRowsFast; ++k) {
+            r8[k] = route_row(my_rows, k0 + k, K, R);
+            any |= r8[k] >= 0;
+        }
+        float acc[kRowsFast];
+#pragma unroll
+        for (int k = 0; k < kRowsFast; ++k) acc[k] = 0.0f;
+        if (any) {
+            for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
+                V gv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t c = c0 + u * kWave + lane;
+                    if (c < c_end) gv[u] = stream_load<VEC>(g_row, c);
+                }
+#pragma unroll
+                for (int kb = 0; kb < kRowsFast; kb += kKBatch) {
+                    V v[kKBatch][U];
+#pragma unroll
+                    for (int kk = 0; kk < kKBatch; ++kk) {
+                        const int r = r8[kb + kk];
+                        if (r < 0) continue;
+                        const uint8_t* src = y + (int64_t)r * row_bytes;
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const int64_t c = c0 + u * kWave + lane;
+                            if (c < c_end) v[kk][u] = stream_load<VEC>(src, c);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        if (c0 + u * kWave + lane >= c_end) continue;
+                        float g[N];
+                        L::unpack(gv[u], g);
+#pragma unroll
+                        for (int kk = 0; kk < kKBatch; ++kk) {
+                            if (r8[kb + kk] < 0) continue;
                             float f[N];
                             L::unpack(v[kk][u], f);
 #pragma unroll
-                            for (int i = 0; i < N; ++i) acc[u][i] = fmaf(w, f[i], acc[u][i]);
+                            for (int i = 0; i < N; ++i) acc[kb + kk] = fmaf(f[i], g[i], acc[kb + kk]);
                         }
                     }
                 }
             }
         }
 #pragma unroll
-        for (int u = 0; u < kCombUnroll; ++u) {
-            const int64_t c = c0 + (int64_t)u * kBlock;
-            if (c < nch) store_vec<VEC>(dst, c, L::pack(acc[u]));
-        }
-    }
-}
-
-constexpr int kWgBatch = 8;  // dots accumulated per pass over the gradient row
-
-template <int DT, int VEC>
-__global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
-                                                       float* __restrict__ wgrad, int64_t nch, int32_t K,
-                                                       const int32_t* __restrict__ slot_row, int64_t static_rows,
-                                                       const int32_t* __restrict__ padded_bins, int32_t E) {
-    using L = Lanes<DT, VEC>;
-    using V = typename L::V;
-    constexpr int N = L::N;
-    constexpr int NW = kBlock / kWave;
-    __shared__ int srow[PEG_MAX_EXPERTS];
-    __shared__ int sk[PEG_MAX_EXPERTS];
-    __shared__ float red[NW][kWgBatch];
-    __shared__ int s_nv;
-    const int64_t t = blockIdx.x;
-    const int64_t R = expert_rows(static_rows, padded_bins, E);
-    // every output of the token starts at 0 (dropped / unrouted stay 0)
-    for (int k = threadIdx.x; k < K; k += kBlock) wgrad[t * K + k] = 0.0f;
-    const int nv = stage_token(t, K, slot_row, nullptr, R, srow, nullptr, sk, &s_nv);
-    if (nv == 0) return;
-    const int64_t row_bytes = nch * VEC;
-    const uint8_t* g_row = grad + t * row_bytes;
-    const int w = threadIdx.x / kWave;
-
-    for (int k0 = 0; k0 < nv; k0 += kWgBatch) {
-        float acc[kWgBatch];
-#pragma unroll
-        for (int kk = 0; kk < kWgBatch; ++kk) acc[kk] = 0.0f;
-        for (int64_t c = threadIdx.x; c < nch; c += kBlock) {
-            float g[N];
-            L::unpack(load_vec<VEC>(g_row, c), g);
-            V v[kWgBatch];
-#pragma unroll
-            for (int kk = 0; kk < kWgBatch; ++kk)
-                if (k0 + kk < nv) v[kk] = load_vec<VEC>(y + (int64_t)srow[k0 + kk] * row_bytes, c);
-#pragma unroll
-            for (int kk = 0; kk < kWgBatch; ++kk) {
-                if (k0 + kk < nv) {
-                    float f[N];
-                    L::unpack(v[kk], f);
-#pragma unroll
-                    for (int i = 0; i < N; ++i) acc[kk] = fmaf(f[i], g[i], acc[kk]);
-                }
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < kWgBatch; ++kk) {
-            const float s = wave_sum(acc[kk]);
-            if (lane_id() == 0) red[w][kk] = s;
+        for (int k = 0; k < kRowsFast; ++k) {
+            if (r8[k] < 0) continue;
+            const float s = wave_sum(acc[k]);
+            if (lane == 0) red[w][k] = s;
         }
         __syncthreads();
-        if (threadIdx.x < kWgBatch && k0 + (int)threadIdx.x < nv) {
+        if (threadIdx.x < kRowsFast && k0 + (int)threadIdx.x < K) {
+            const int k = threadIdx.x;
             float s = 0.0f;
+            if (route_row(my_rows, k0 + k, K, R) >= 0) {
 #pragma unroll
-            for (int i = 0; i < NW; ++i) s += red[i][threadIdx.x];
-            wgrad[t * K + sk[k0 + threadIdx.x]] = s;
+                for (int i = 0; i < NW; ++i) s += red[i][k];
+            }
+            wgrad[t * K + k0 + k] = s;  // 0 for dropped or unrouted assignments
         }
         __syncthreads();
     }
@@ -208,44 +250,55 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
     return PEG_OK;
 }
 
+// Vectors per lane per pass: the quarter in one pass when it fits in 2.
+static int pass_vectors(int64_t quarter) { return lanes_per_pass(quarter) >= 2 ? 2 : 1; }
+
+template <int DT, int VEC>
+static peg_status combine_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
+                              int64_t q, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
+    if (u == 1)
+        return launch(combine_kernel<DT, VEC, 1>, grid, dim3(kBlock), 0, s, y, out, nch, q, K, slot_row, w,
+                      ra.static_rows, ra.padded_bins, E);
+    return launch(combine_kernel<DT, VEC, 2>, grid, dim3(kBlock), 0, s, y, out, nch, q, K, slot_row, w,
+                  ra.static_rows, ra.padded_bins, E);
+}
+
 template <int DT>
 static peg_status combine_dispatch(int vec, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
                                    int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
+    const int64_t q = wave_quarter(nch);
+    const int u = pass_vectors(q);
     switch (vec) {
-        case 16:
-            return launch(combine_kernel<DT, 16>, grid, dim3(kBlock), 0, s, y, out, nch, K, slot_row, w,
-                          ra.static_rows, ra.padded_bins, E);
-        case 8:
-            return launch(combine_kernel<DT, 8>, grid, dim3(kBlock), 0, s, y, out, nch, K, slot_row, w,
-                          ra.static_rows, ra.padded_bins, E);
-        case 4:
-            return launch(combine_kernel<DT, 4>, grid, dim3(kBlock), 0, s, y, out, nch, K, slot_row, w,
-                          ra.static_rows, ra.padded_bins, E);
+        case 16: return combine_vec<DT, 16>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
+        case 8: return combine_vec<DT, 8>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
+        case 4: return combine_vec<DT, 4>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
         default:
-            if constexpr (Elem<DT>::bytes == 2)
-                return launch(combine_kernel<DT, 2>, grid, dim3(kBlock), 0, s, y, out, nch, K, slot_row, w,
-                              ra.static_rows, ra.padded_bins, E);
+            if constexpr (Elem<DT>::bytes == 2) return combine_vec<DT, 2>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
             return PEG_ERR_ALIGNMENT;
     }
+}
+
+template <int DT, int VEC>
+static peg_status wgrad_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg,
+                            int64_t nch, int64_t q, int32_t K, const int32_t* slot_row, RowArgs ra, int32_t E) {
+    if (u == 1)
+        return launch(wgrad_kernel<DT, VEC, 1>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, K, slot_row,
+                      ra.static_rows, ra.padded_bins, E);
+    return launch(wgrad_kernel<DT, VEC, 2>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, K, slot_row,
+                  ra.static_rows, ra.padded_bins, E);
 }
 
 template <int DT>
 static peg_status wgrad_dispatch(int vec, dim3 grid, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg,
                                  int64_t nch, int32_t K, const int32_t* slot_row, RowArgs ra, int32_t E) {
+    const int64_t q = wave_quarter(nch);
+    const int u = pass_vectors(q);
     switch (vec) {
-        case 16:
-            return launch(wgrad_kernel<DT, 16>, grid, dim3(kBlock), 0, s, y, g, wg, nch, K, slot_row,
-                          ra.static_rows, ra.padded_bins, E);
-        case 8:
-            return launch(wgrad_kernel<DT, 8>, grid, dim3(kBlock), 0, s, y, g, wg, nch, K, slot_row,
-                          ra.static_rows, ra.padded_bins, E);
-        case 4:
-            return launch(wgrad_kernel<DT, 4>, grid, dim3(kBlock), 0, s, y, g, wg, nch, K, slot_row,
-                          ra.static_rows, ra.padded_bins, E);
+        case 16: return wgrad_vec<DT, 16>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
+        case 8: return wgrad_vec<DT, 8>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
+        case 4: return wgrad_vec<DT, 4>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
         default:
-            if constexpr (Elem<DT>::bytes == 2)
-                return launch(wgrad_kernel<DT, 2>, grid, dim3(kBlock), 0, s, y, g, wg, nch, K, slot_row,
-                              ra.static_rows, ra.padded_bins, E);
+            if constexpr (Elem<DT>::bytes == 2) return wgrad_vec<DT, 2>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
             return PEG_ERR_ALIGNMENT;
     }
 }

@@ -10,9 +10,11 @@
 // How (MI355X design, not the pages' Ascend sub-block buffering):
 //   * token-major: one block per token reads the token row once from HBM
 //     into VGPRs (16-byte lanes) and stores it to each of its <= K rows, so
-//     the source is read exactly once however many experts it goes to;
-//   * the rows of a token come from the assignment -> row map (slot_row)
-//     staged in LDS;
+//     the source is read exactly once however many experts it goes to; each
+//     of the 4 waves owns a contiguous quarter of the row;
+//   * the rows of a token come from the assignment -> row map (slot_row) by
+//     wave-uniform scalar loads, so the row loads issue at once, with no LDS
+//     staging or barrier in front of them;
 //   * in the same launch, trailing "gap" blocks write zeros into the unused
 //     capacity / padding rows only (each gap of an expert is one contiguous
 //     byte range), so no row is written twice and no memset pass is needed.
@@ -21,11 +23,11 @@
 
 namespace peg {
 
-constexpr int kGatherUnroll = 4;
-
-template <int VEC>
+// Columns of a token row are split into 4 contiguous quarters, one per wave
+// of the block; a wave moves its quarter in passes of 64 lanes x U vectors.
+template <int VEC, int U>
 __global__ __launch_bounds__(kBlock) void gather_kernel(
-    const uint8_t* __restrict__ x, uint8_t* __restrict__ out, int64_t nch, int32_t K,
+    const uint8_t* __restrict__ x, uint8_t* __restrict__ out, int64_t nch, int64_t quarter, int32_t K,
     const int32_t* __restrict__ slot_row, int64_t out_rows, int32_t layout, int32_t E, int32_t capacity,
     const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int64_t token_blocks,
     uint32_t* __restrict__ err_flag) {
@@ -33,46 +35,57 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     const int64_t row_bytes = nch * VEC;
 
     if ((int64_t)blockIdx.x < token_blocks) {
-        // ---------------- token rows -> their expert rows ----------------
-        __shared__ int srow[PEG_MAX_EXPERTS];
-        __shared__ int s_nv;
+        // ---------------- token row -> its expert rows ----------------
         const int64_t t = blockIdx.x;
-        bool overflow = false;
-        for (int k = threadIdx.x; k < K; k += kBlock) {
-            int r = slot_row[t * K + k];
-            if (r >= out_rows) {
-                overflow = true;
-                r = -1;
-            }
-            srow[k] = r;
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        const int lane = lane_id();
+        const int64_t c_begin = w * quarter;
+        const int64_t c_end = c_begin + quarter < nch ? c_begin + quarter : nch;
+        const int32_t* my_rows = slot_row + t * K;
+        // rows of the token: wave-uniform loads (scalar unit), K <= 8 kept in SGPRs
+        int r8[kRowsFast];
+#pragma unroll
+        for (int k = 0; k < kRowsFast; ++k) r8[k] = k < K ? my_rows[k] : -1;
+        bool any = false, over = false;
+#pragma unroll
+        for (int k = 0; k < kRowsFast; ++k) {
+            if (r8[k] >= out_rows) over = true;
+            any |= r8[k] >= 0 && r8[k] < out_rows;
         }
-        if (overflow && err_flag) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
-        __syncthreads();
-        if (threadIdx.x == 0) {  // keep the valid rows, in k order
-            int nv = 0;
-            for (int k = 0; k < K; ++k) {
-                int r = srow[k];
-                if (r >= 0) srow[nv++] = r;
-            }
-            s_nv = nv;
+        for (int k = kRowsFast; k < K; ++k) {
+            const int r = my_rows[k];
+            if (r >= out_rows) over = true;
+            any |= r >= 0 && r < out_rows;
         }
-        __syncthreads();
-        const int nv = s_nv;
-        if (nv == 0) return;  // token fully dropped: its row is never read
+        if (over && err_flag && threadIdx.x == 0) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
+        if (!any) return;  // token fully dropped: its row is never read
         const uint8_t* src = x + t * row_bytes;
-        for (int64_t c0 = threadIdx.x; c0 < nch; c0 += (int64_t)kBlock * kGatherUnroll) {
-            V v[kGatherUnroll];
+        for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
+            V v[U];
 #pragma unroll
-            for (int u = 0; u < kGatherUnroll; ++u) {
-                const int64_t c = c0 + (int64_t)u * kBlock;
-                if (c < nch) v[u] = load_vec<VEC>(src, c);
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u * kWave + lane;
+                if (c < c_end) v[u] = stream_load<VEC>(src, c);
             }
-            for (int j = 0; j < nv; ++j) {
-                uint8_t* dst = out + (int64_t)srow[j] * row_bytes;
 #pragma unroll
-                for (int u = 0; u < kGatherUnroll; ++u) {
-                    const int64_t c = c0 + (int64_t)u * kBlock;
-                    if (c < nch) store_vec<VEC>(dst, c, v[u]);
+            for (int k = 0; k < kRowsFast; ++k) {
+                const int r = r8[k];
+                if (r < 0 || r >= out_rows) continue;
+                uint8_t* dst = out + (int64_t)r * row_bytes;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t c = c0 + u * kWave + lane;
+                    if (c < c_end) stream_store<VEC>(dst, c, v[u]);
+                }
+            }
+            for (int k = kRowsFast; k < K; ++k) {
+                const int r = my_rows[k];
+                if (r < 0 || r >= out_rows) continue;
+                uint8_t* dst = out + (int64_t)r * row_bytes;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t c = c0 + u * kWave + lane;
+                    if (c < c_end) stream_store<VEC>(dst, c, v[u]);
                 }
             }
         }
@@ -137,8 +150,34 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     for (; u < hi; u += kBlock) {
         while ((int64_t)gpre[e + 1] * nch <= u) ++e;
         const int64_t dst_unit = (int64_t)gstart[e] * nch + (u - (int64_t)gpre[e] * nch);
-        store_vec<VEC>(out, dst_unit, z);
+        stream_store<VEC>(out, dst_unit, z);
     }
+}
+
+struct GatherArgs {
+    const uint8_t* x;
+    uint8_t* out;
+    int64_t nch, quarter;
+    int32_t K;
+    const int32_t* slot_row;
+    int64_t out_rows;
+    int32_t layout, E, capacity;
+    const int32_t* bins;
+    const int32_t* padded_bins;
+    int64_t token_blocks;
+    uint32_t* err_flag;
+};
+
+template <int VEC>
+static peg_status gather_launch(int u, dim3 grid, hipStream_t s, const GatherArgs& a) {
+#define PEG_GATHER_U(UU)                                                                                        \
+    return launch(gather_kernel<VEC, UU>, grid, dim3(kBlock), 0, s, a.x, a.out, a.nch, a.quarter, a.K,        \
+                  a.slot_row, a.out_rows, a.layout, a.E, a.capacity, a.bins, a.padded_bins, a.token_blocks,    \
+                  a.err_flag)
+    if (u == 1) PEG_GATHER_U(1);
+    if (u == 2) PEG_GATHER_U(2);
+    PEG_GATHER_U(4);
+#undef PEG_GATHER_U
 }
 
 // Zero-fill blocks: enough that each writes a few hundred KB at most.
@@ -180,19 +219,15 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
     const int64_t nch = row_bytes / vec;
     const int64_t nz = gap_blocks(out_rows, nch, vec);
     const dim3 grid((unsigned)(T + nz));
+    const int64_t quarter = wave_quarter(nch);
+    const int u = lanes_per_pass(quarter);
+    const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, quarter, K, slot_row, out_rows, layout, E, capacity,
+                       bins, padded_bins, T, err_flag};
     switch (vec) {
-        case 16:
-            return launch(gather_kernel<16>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
-                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
-        case 8:
-            return launch(gather_kernel<8>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
-                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
-        case 4:
-            return launch(gather_kernel<4>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
-                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
-        default:
-            return launch(gather_kernel<2>, grid, dim3(kBlock), 0, s, (const uint8_t*)x, (uint8_t*)out, nch, K,
-                          slot_row, out_rows, layout, E, capacity, bins, padded_bins, T, err_flag);
+        case 16: return gather_launch<16>(u, grid, s, a);
+        case 8: return gather_launch<8>(u, grid, s, a);
+        case 4: return gather_launch<4>(u, grid, s, a);
+        default: return gather_launch<2>(u, grid, s, a);
     }
 }
 

@@ -10,6 +10,7 @@
 namespace peg {
 
 constexpr int kWave = 64;
+constexpr int kRowsFast = 8;  // routes per token held in scalar registers (more are looped)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -21,6 +22,22 @@ template <> struct VecOf<8> { using T = u32x2; };
 template <> struct VecOf<4> { using T = uint32_t; };
 template <> struct VecOf<2> { using T = uint16_t; };
 
+// Build-time tuning knobs (defaults are the measured best on MI355X):
+//   PEG_NT_LOAD  - streamed row loads carry the nontemporal hint (+4-6% on
+//                  every row kernel);
+//   PEG_NT_STORE - the gathers' row stores carry it too (off: it costs the
+//                  write-bound gathers up to 17%);
+//   PEG_NT_STORE_COMBINE - the combine's output stores carry it (+7-9%).
+#ifndef PEG_NT_LOAD
+#define PEG_NT_LOAD 1
+#endif
+#ifndef PEG_NT_STORE
+#define PEG_NT_STORE 0
+#endif
+#ifndef PEG_NT_STORE_COMBINE
+#define PEG_NT_STORE_COMBINE 1
+#endif
+
 template <int VEC>
 __device__ __forceinline__ typename VecOf<VEC>::T load_vec(const uint8_t* base, int64_t unit) {
     return reinterpret_cast<const typename VecOf<VEC>::T*>(base)[unit];
@@ -29,6 +46,23 @@ __device__ __forceinline__ typename VecOf<VEC>::T load_vec(const uint8_t* base, 
 template <int VEC>
 __device__ __forceinline__ void store_vec(uint8_t* base, int64_t unit, typename VecOf<VEC>::T v) {
     reinterpret_cast<typename VecOf<VEC>::T*>(base)[unit] = v;
+}
+
+// Row streaming: data touched once per launch (token rows, expert rows,
+// gradient rows, outputs).
+template <int VEC>
+__device__ __forceinline__ typename VecOf<VEC>::T stream_load(const uint8_t* base, int64_t unit) {
+#if PEG_NT_LOAD
+    return __builtin_nontemporal_load(reinterpret_cast<const typename VecOf<VEC>::T*>(base) + unit);
+#else
+    return load_vec<VEC>(base, unit);
+#endif
+}
+
+template <int VEC, bool NT = PEG_NT_STORE>
+__device__ __forceinline__ void stream_store(uint8_t* base, int64_t unit, typename VecOf<VEC>::T v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<typename VecOf<VEC>::T*>(base) + unit);
+    else store_vec<VEC>(base, unit, v);
 }
 
 template <int VEC>

@@ -35,6 +35,21 @@ inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, con
     return 0;
 }
 
+// A row of nch vectors is split over the 4 waves of a block: each wave owns
+// a contiguous quarter, rounded up to 8 vectors (128 bytes at 16-byte
+// vectors) so that every wave starts on a cache-line boundary.
+inline int64_t wave_quarter(int64_t nch) {
+    const int64_t q = (nch + 3) / 4;
+    return (q + 7) & ~int64_t(7);
+}
+
+// Vectors per lane per pass (1, 2 or 4) so that one pass covers a quarter
+// when it can.
+inline int lanes_per_pass(int64_t quarter) {
+    const int64_t p = (quarter + 63) / 64;
+    return p <= 1 ? 1 : (p <= 2 ? 2 : 4);
+}
+
 // Tiles of the routing preparation: 256 threads x ITEMS assignments. The
 // per-chunk count table of a tile (4 * ITEMS chunks of 64 x E ints) stays
 // within 32 KB of LDS.

@@ -8,39 +8,176 @@
 // "Build Triton-Ascend Binned MoE Routing", Workflow steps 1-3 (inclusive
 // bins, capacity cut-off) and Implementation Pattern.
 //
-// Three launches, no global atomics, deterministic:
-//   1. tile_hist   : one block per tile of 256*ITEMS assignment ids; LDS
-//                    histogram of its expert ids -> counts[e][tile].
-//   2. tile_scan   : one 1024-thread block; exclusive scan of counts in
-//                    expert-major order, which is directly the first sorted
-//                    position of (expert e, tile) -> bins, padded_bins.
-//   3. tile_place  : every tile re-reads its ids; a wave64 "multisplit"
-//                    (ballots over the bits of the expert id) gives each id
-//                    its rank among equal ids of its 64-id chunk; per-chunk
-//                    counts scanned in LDS give the rank inside the tile.
-//                    Position = tile base + chunk prefix + rank, which keeps
-//                    ascending assignment id inside each expert (stable).
+// Ranking inside a 64-id chunk is a wave64 "multisplit": ballots over the bits
+// of the expert id give every lane the mask of lanes holding the same expert;
+// its rank is the popcount of that mask below the lane. Per-(chunk, expert)
+// counts are then scanned over chunks in LDS (one wave64 scan per expert),
+// which keeps ascending assignment id inside every expert (a stable sort).
+// No global atomics; the result is deterministic.
+//
+// Two paths:
+//   small: T*K <= 16384 and its count table fits in LDS -> one 1024-thread
+//          block does everything (histogram, scans, placement) in one launch;
+//   tiled: tiles of 256*ITEMS ids; three launches (tile histograms, one
+//          expert-major scan that yields each (expert, tile) base position
+//          and the bins, placement).
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
 namespace peg {
+
+// Mask of the lanes of this wave whose expert id equals this lane's.
+__device__ __forceinline__ uint64_t same_expert_mask(int v, bool valid, int nbits) {
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (v >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        same &= bit ? ones : ~ones;
+    }
+    return same;
+}
+
+// In-place exclusive scan over the NCH chunks of every expert column of the
+// LDS table cnt[NCH][E]; one wave per expert (waves stride over experts),
+// 64 chunks per pass. tot[e] (optional) receives each expert's total.
+// Must be called by the whole block; ends with a barrier.
+template <int NW>
+__device__ __forceinline__ void scan_chunks(int* cnt, int nch, int E, int* tot) {
+    const int lane = lane_id();
+    const int w = threadIdx.x / kWave;
+    for (int e = w; e < E; e += NW) {
+        int carry = 0;
+        for (int c0 = 0; c0 < nch; c0 += kWave) {
+            const int c = c0 + lane;
+            const int v = c < nch ? cnt[c * E + e] : 0;
+            const int inc = wave_inclusive_scan(v);
+            if (c < nch) cnt[c * E + e] = carry + inc - v;
+            carry += __shfl(inc, kWave - 1, kWave);
+        }
+        if (tot && lane == 0) tot[e] = carry;
+    }
+    __syncthreads();
+}
+
+// Row of sorted position pos of expert e ([BIN]/[PAD] Implementation Pattern).
+__device__ __forceinline__ int position_row(int layout, int e, int capacity, int offset, int padded_start) {
+    if (layout == PEG_BINNED) return offset < capacity ? e * capacity + offset : -1;
+    return padded_start + offset;
+}
+
+// ---------------------------------------------------------------------------
+// Small path: one block of 1024 threads, ITEMS ids per thread.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int64_t kSmallMaxIds = 16384;
+constexpr size_t kSmallMaxTable = 48 * 1024;
+
+template <int ITEMS>
+__global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
+    const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, int32_t pad_multiple, int32_t layout,
+    int32_t capacity, int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
+    int32_t* __restrict__ tokens_per_expert, int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
+    int32_t* __restrict__ slot_row) {
+    constexpr int NCH = ITEMS * kSmallWaves;
+    extern __shared__ int lds[];
+    int* cnt = lds;                 // [NCH][E]
+    int* start = cnt + NCH * E;     // [E] first sorted position of each expert
+    int* pstart = start + E;        // [E] first padded row of each expert
+    int* tot = pstart + E;          // [E] count of each expert
+    __shared__ int scratch[kSmallWaves];
+    __shared__ int s_n;
+
+    // ids first: their loads overlap the table clearing
+    int v[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int64_t a = (int64_t)j * kSmallThreads + threadIdx.x;
+        v[j] = a < total ? top[a] : -1;
+    }
+    for (int i = threadIdx.x; i < NCH * E; i += kSmallThreads) cnt[i] = 0;
+    __syncthreads();
+
+    const int w = threadIdx.x / kWave;
+    int rank[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const bool valid = (unsigned)v[j] < (unsigned)E;
+        const uint64_t same = same_expert_mask(v[j], valid, nbits);
+        rank[j] = __popcll(same & lanes_below());
+        if (valid && rank[j] == 0) cnt[(j * kSmallWaves + w) * E + v[j]] = __popcll(same);
+        if (!valid) v[j] = -1;
+    }
+    __syncthreads();
+    scan_chunks<kSmallWaves>(cnt, NCH, E, tot);
+
+    // bins: inclusive scan of the counts over experts (E <= 1024 = threads)
+    {
+        const int e = threadIdx.x;
+        const int count = e < E ? tot[e] : 0;
+        int n;
+        const int pre = block_exclusive_scan<kSmallThreads>(count, scratch, &n);
+        if (e < E) {
+            start[e] = pre;
+            bins[e] = pre + count;
+            if (tokens_per_expert) tokens_per_expert[e] = count;
+        }
+        if (e == 0) s_n = n;
+        if (padded_bins) {
+            const int rounded = e < E ? ((count + pad_multiple - 1) / pad_multiple) * pad_multiple : 0;
+            int ptotal;
+            const int ppre = block_exclusive_scan<kSmallThreads>(rounded, scratch, &ptotal);
+            if (e < E) {
+                pstart[e] = ppre;
+                padded_bins[e] = ppre + rounded;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int n = s_n;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int64_t a = (int64_t)j * kSmallThreads + threadIdx.x;
+        if (a >= total) continue;
+        const int e = v[j];
+        if (e >= 0) {
+            const int pos = start[e] + cnt[(j * kSmallWaves + w) * E + e] + rank[j];
+            indices[pos] = (int32_t)a;
+            bin_ids[pos] = e;
+            if (slot_row)
+                slot_row[a] = position_row(layout, e, capacity, pos - start[e], padded_bins ? pstart[e] : 0);
+        } else if (slot_row) {
+            slot_row[a] = -1;
+        }
+        if (a >= n) {
+            indices[a] = -1;
+            bin_ids[a] = -1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled path.
+// ---------------------------------------------------------------------------
 
 template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void tile_hist_kernel(const int32_t* __restrict__ top, int64_t total,
                                                            int32_t E, int64_t ntiles,
                                                            int32_t* __restrict__ counts) {
     __shared__ int hist[PEG_MAX_EXPERTS];
-    for (int e = threadIdx.x; e < E; e += kBlock) hist[e] = 0;
-    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * (kBlock * ITEMS);
+    int v[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        int64_t a = base + j * kBlock + threadIdx.x;
-        if (a < total) {
-            int v = top[a];
-            if ((unsigned)v < (unsigned)E) atomicAdd(&hist[v], 1);
-        }
+        const int64_t a = base + j * kBlock + threadIdx.x;
+        v[j] = a < total ? top[a] : -1;
     }
+    for (int e = threadIdx.x; e < E; e += kBlock) hist[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+        if ((unsigned)v[j] < (unsigned)E) atomicAdd(&hist[v[j]], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kBlock) counts[(int64_t)e * ntiles + blockIdx.x] = hist[e];
 }
@@ -103,58 +240,55 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
     const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, const int32_t* __restrict__ base_pos,
     int64_t ntiles, const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int32_t layout,
     int32_t capacity, int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids, int32_t* __restrict__ slot_row) {
-    constexpr int NCH = ITEMS * (kBlock / kWave);  // 64-id chunks per tile
-    extern __shared__ int chunk_cnt[];              // [NCH][E]
-    for (int i = threadIdx.x; i < NCH * E; i += kBlock) chunk_cnt[i] = 0;
-    __syncthreads();
+    constexpr int NW = kBlock / kWave;
+    constexpr int NCH = ITEMS * NW;  // 64-id chunks per tile
+    extern __shared__ int lds[];
+    int* cnt = lds;              // [NCH][E]
+    int* tbase = cnt + NCH * E;  // [E] first sorted position of (e, this tile)
+    int* start = tbase + E;      // [E] first sorted position of e
+    int* pstart = start + E;     // [E] first padded row of e
+    __shared__ int s_n;
 
-    const int w = threadIdx.x / kWave;
     const int64_t base = (int64_t)blockIdx.x * (kBlock * ITEMS);
-    int ex[ITEMS], rank[ITEMS];
+    int v[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const int64_t a = base + j * kBlock + threadIdx.x;
-        const int v = a < total ? top[a] : -1;
-        const bool valid = (unsigned)v < (unsigned)E;
-        uint64_t same = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (v >> b) & 1;
-            const uint64_t ones = __ballot(valid && bit);
-            same &= bit ? ones : ~ones;
-        }
-        ex[j] = valid ? v : -1;
-        rank[j] = __popcll(same & lanes_below());
-        if (valid && rank[j] == 0) chunk_cnt[(j * (kBlock / kWave) + w) * E + v] = __popcll(same);
+        v[j] = a < total ? top[a] : -1;
     }
-    __syncthreads();
     for (int e = threadIdx.x; e < E; e += kBlock) {
-        int run = 0;
-        for (int c = 0; c < NCH; ++c) {
-            int t = chunk_cnt[c * E + e];
-            chunk_cnt[c * E + e] = run;
-            run += t;
-        }
+        tbase[e] = base_pos[(int64_t)e * ntiles + blockIdx.x];
+        start[e] = e ? bins[e - 1] : 0;
+        pstart[e] = (padded_bins && e) ? padded_bins[e - 1] : 0;
     }
+    if (threadIdx.x == 0) s_n = bins[E - 1];
+    for (int i = threadIdx.x; i < NCH * E; i += kBlock) cnt[i] = 0;
     __syncthreads();
 
-    const int n = bins[E - 1];
+    const int w = threadIdx.x / kWave;
+    int rank[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const bool valid = (unsigned)v[j] < (unsigned)E;
+        const uint64_t same = same_expert_mask(v[j], valid, nbits);
+        rank[j] = __popcll(same & lanes_below());
+        if (valid && rank[j] == 0) cnt[(j * NW + w) * E + v[j]] = __popcll(same);
+        if (!valid) v[j] = -1;
+    }
+    __syncthreads();
+    scan_chunks<NW>(cnt, NCH, E, nullptr);
+
+    const int n = s_n;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const int64_t a = base + j * kBlock + threadIdx.x;
         if (a >= total) continue;
-        const int e = ex[j];
+        const int e = v[j];
         if (e >= 0) {
-            const int pos = base_pos[(int64_t)e * ntiles + blockIdx.x] +
-                            chunk_cnt[(j * (kBlock / kWave) + w) * E + e] + rank[j];
+            const int pos = tbase[e] + cnt[(j * NW + w) * E + e] + rank[j];
             indices[pos] = (int32_t)a;
             bin_ids[pos] = e;
-            if (slot_row) {
-                const int offset = pos - (e ? bins[e - 1] : 0);
-                int row;
-                if (layout == PEG_BINNED) row = offset < capacity ? e * capacity + offset : -1;
-                else row = (e ? padded_bins[e - 1] : 0) + offset;
-                slot_row[a] = row;
-            }
+            if (slot_row) slot_row[a] = position_row(layout, e, capacity, pos - start[e], pstart[e]);
         } else if (slot_row) {
             slot_row[a] = -1;
         }
@@ -165,22 +299,42 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
     }
 }
 
-template <int ITEMS>
-static peg_status prep_launch(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
-                              int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe,
-                              int32_t* bins, int32_t* padded_bins, int32_t* slot_row, int32_t* counts,
-                              hipStream_t s) {
-    const int64_t ntiles = prep_tiles(total, E);
+static int id_bits(int E) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
+    return nbits;
+}
+
+template <int ITEMS>
+static peg_status prep_tiled(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                             int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                             int32_t* padded_bins, int32_t* slot_row, int32_t* counts, hipStream_t s) {
+    const int64_t ntiles = prep_tiles(total, E);
     PEG_CHECK(launch(tile_hist_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), 0, s, top, total, E, ntiles,
                      counts));
     PEG_CHECK(launch(tile_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E, pad_multiple, tpe,
                      bins, padded_bins));
-    const size_t lds = (size_t)ITEMS * (kBlock / kWave) * E * sizeof(int);
-    PEG_CHECK(launch(tile_place_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,
-                     nbits, counts, ntiles, bins, padded_bins, layout, capacity, indices, bin_ids, slot_row));
-    return PEG_OK;
+    const size_t lds = ((size_t)ITEMS * (kBlock / kWave) * E + 3 * (size_t)E) * sizeof(int);
+    return launch(tile_place_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,
+                  id_bits(E), counts, ntiles, bins, padded_bins, layout, capacity, indices, bin_ids, slot_row);
+}
+
+template <int ITEMS>
+static peg_status prep_small(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                             int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                             int32_t* padded_bins, int32_t* slot_row, hipStream_t s) {
+    const size_t lds = ((size_t)ITEMS * kSmallWaves * E + 3 * (size_t)E) * sizeof(int);
+    return launch(prep_small_kernel<ITEMS>, dim3(1), dim3(kSmallThreads), lds, s, top, total, E, id_bits(E),
+                  pad_multiple, layout, capacity, indices, bin_ids, tpe, bins, padded_bins, slot_row);
+}
+
+// Ids per thread of the small path, 0 if it does not apply.
+static int small_items(int64_t total, int32_t E) {
+    if (total > kSmallMaxIds) return 0;
+    int items = 1;
+    while ((int64_t)items * kSmallThreads < total) items <<= 1;
+    if ((size_t)items * kSmallWaves * E * sizeof(int) > kSmallMaxTable) return 0;
+    return items;
 }
 
 }  // namespace peg
@@ -205,14 +359,27 @@ PEG_API peg_status peg_route_prep(const int32_t* top_experts, int64_t T, int32_t
     if (!ws) return PEG_ERR_WORKSPACE;
     if (ws_bytes < ws_need(T, K, E)) return PEG_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (small_items(total, E)) {
+        case 1: return prep_small<1>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 2: return prep_small<2>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 4: return prep_small<4>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 8: return prep_small<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 16: return prep_small<16>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                       tokens_per_expert, bins, padded_bins, slot_row, s);
+        default: break;
+    }
     int32_t* counts = reinterpret_cast<int32_t*>(ws);
     const int items = prep_items(E);
     if (items == 8)
-        return prep_launch<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                              tokens_per_expert, bins, padded_bins, slot_row, counts, s);
+        return prep_tiled<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                             tokens_per_expert, bins, padded_bins, slot_row, counts, s);
     if (items == 4)
-        return prep_launch<4>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                              tokens_per_expert, bins, padded_bins, slot_row, counts, s);
-    return prep_launch<2>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                          tokens_per_expert, bins, padded_bins, slot_row, counts, s);
+        return prep_tiled<4>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                             tokens_per_expert, bins, padded_bins, slot_row, counts, s);
+    return prep_tiled<2>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                         tokens_per_expert, bins, padded_bins, slot_row, counts, s);
 }
