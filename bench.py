@@ -60,7 +60,21 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 1 GiB device-to-device copies (reference for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(torch):
+    """Plain copies of known size: what FETCH_SIZE / WRITE_SIZE read for
+    1 GiB in and 1 GiB out calibrates the counters of the data-path kernels."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    for i in range(4):
+        bufs[i % 2].copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
 
 
 class HipEvents:
@@ -261,6 +275,10 @@ def main():
     import torch
     import padded_expert_gather_amd as peg
     import workloads as W
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

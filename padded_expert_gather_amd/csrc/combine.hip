@@ -10,12 +10,13 @@
 //   wgrad: wgrad[a] = <y[row(a)], grad[a / K]> for kept a, else 0 (Workflow
 //     step 6 of both pages; fp32 accumulation per their Ascend Guardrails).
 //
-// How: token-major. One block per token; the token's rows (and weights) come
-// in by wave-uniform scalar loads, and each of the 4 waves streams its
-// quarter of the H columns in 16-byte lanes: every kept expert row is read
+// How: token-major. The token's rows (and weights) come in by wave-uniform
+// scalar loads, and each of the token's waves streams its slice of the H
+// columns in 16-byte lanes: every kept expert row is read
 // once, the output row (combine) is written once, the gradient row (wgrad)
 // is read once for all K dots. Accumulation is fp32 FMA; the wgrad dots
-// finish with a wave64 butterfly and a 4-wave sum in LDS. Rows that are
+// finish with a wave64 butterfly and a sum over the token's waves in LDS.
+// Rows that are
 // unused capacity, padding or dropped are never read.
 #include "peg_device.hpp"
 #include "peg_host.hpp"
@@ -39,22 +40,23 @@ __device__ __forceinline__ int route_row(const int32_t* __restrict__ rows, int k
     return (r < 0 || r >= R) ? -1 : r;
 }
 
-// Columns of a token row are split into 4 contiguous quarters, one per wave
-// of the block; a wave covers its quarter in passes of 64 lanes x U vectors.
-template <int DT, int VEC, int U>
+// The columns of a token row are split into WPT contiguous slices, one per
+// wave; a wave covers its slice in passes of 64 lanes x U vectors.
+template <int DT, int VEC, int U, int WPT>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restrict__ y, uint8_t* __restrict__ out,
-                                                         int64_t nch, int64_t quarter, int32_t K,
+                                                         int64_t nch, int64_t slice, int64_t T, int32_t K,
                                                          const int32_t* __restrict__ slot_row,
                                                          const float* __restrict__ weights, int64_t static_rows,
                                                          const int32_t* __restrict__ padded_bins, int32_t E) {
     using L = Lanes<DT, VEC>;
     using V = typename L::V;
     constexpr int N = L::N;
-    const int64_t t = blockIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t t = (int64_t)blockIdx.x * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+    if (t >= T) return;  // no barrier in this kernel
     const int lane = lane_id();
-    const int64_t c_begin = w * quarter;
-    const int64_t c_end = c_begin + quarter < nch ? c_begin + quarter : nch;
+    const int64_t c_begin = (w % WPT) * slice;
+    const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
     const int64_t R = expert_rows(static_rows, padded_bins, E);
     const int32_t* my_rows = slot_row + t * K;
     const float* my_w = weights ? weights + t * K : nullptr;
@@ -127,13 +129,13 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     }
 }
 
-// wgrad: block per token, each wave dots its quarter of the columns for up
-// to 8 routes at a time; partial dots finish with a wave64 butterfly and a
-// 4-wave sum in LDS.
-template <int DT, int VEC, int U>
+// wgrad: each wave dots its slice of the token's columns for up to 8 routes
+// at a time; partial dots finish with a wave64 butterfly and a sum over the
+// token's WPT waves in LDS.
+template <int DT, int VEC, int U, int WPT>
 __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
-                                                       float* __restrict__ wgrad, int64_t nch, int64_t quarter,
-                                                       int32_t K, const int32_t* __restrict__ slot_row,
+                                                       float* __restrict__ wgrad, int64_t nch, int64_t slice,
+                                                       int64_t T, int32_t K, const int32_t* __restrict__ slot_row,
                                                        int64_t static_rows, const int32_t* __restrict__ padded_bins,
                                                        int32_t E) {
     using L = Lanes<DT, VEC>;
@@ -141,22 +143,24 @@ __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict
     constexpr int N = L::N;
     constexpr int NW = kBlock / kWave;
     __shared__ float red[NW][kRowsFast];
-    const int64_t t = blockIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    constexpr int TPB = TokenMap<WPT>::kTokensPerBlock;
+    const int64_t t = (int64_t)blockIdx.x * TPB + w / WPT;
+    const bool active = t < T;  // every wave still takes part in the barriers
     const int lane = lane_id();
-    const int64_t c_begin = w * quarter;
-    const int64_t c_end = c_begin + quarter < nch ? c_begin + quarter : nch;
+    const int64_t c_begin = (w % WPT) * slice;
+    const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
     const int64_t R = expert_rows(static_rows, padded_bins, E);
-    const int32_t* my_rows = slot_row + t * K;
+    const int32_t* my_rows = slot_row + (active ? t : 0) * K;
     const int64_t row_bytes = nch * VEC;
-    const uint8_t* g_row = grad + t * row_bytes;
+    const uint8_t* g_row = grad + (active ? t : 0) * row_bytes;
 
     for (int k0 = 0; k0 < K; k0 += kRowsFast) {
         int r8[kRowsFast];
         bool any = false;
 #pragma unroll
         for (int k = 0; k < kRowsFast; ++k) {
-            r8[k] = route_row(my_rows, k0 + k, K, R);
+            r8[k] = active ? route_row(my_rows, k0 + k, K, R) : -1;
             any |= r8[k] >= 0;
         }
         float acc[kRowsFast];
@@ -207,17 +211,21 @@ __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict
             const float s = wave_sum(acc[k]);
             if (lane == 0) red[w][k] = s;
         }
-        __syncthreads();
-        if (threadIdx.x < kRowsFast && k0 + (int)threadIdx.x < K) {
-            const int k = threadIdx.x;
-            float s = 0.0f;
-            if (route_row(my_rows, k0 + k, K, R) >= 0) {
+        lds_barrier();
+        if (threadIdx.x < TPB * kRowsFast) {
+            const int tl = threadIdx.x / kRowsFast;
+            const int k = threadIdx.x % kRowsFast;
+            const int64_t tt = (int64_t)blockIdx.x * TPB + tl;
+            if (tt < T && k0 + k < K) {
+                float s = 0.0f;
+                if (route_row(slot_row + tt * K, k0 + k, K, R) >= 0) {
 #pragma unroll
-                for (int i = 0; i < NW; ++i) s += red[i][k];
+                    for (int i = 0; i < WPT; ++i) s += red[tl * WPT + i][k];
+                }
+                wgrad[tt * K + k0 + k] = s;  // 0 for dropped or unrouted assignments
             }
-            wgrad[t * K + k0 + k] = s;  // 0 for dropped or unrouted assignments
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -250,55 +258,85 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
     return PEG_OK;
 }
 
-// Vectors per lane per pass: the quarter in one pass when it fits in 2.
-static int pass_vectors(int64_t quarter) { return lanes_per_pass(quarter) >= 2 ? 2 : 1; }
+#ifndef PEG_COMBINE_UMAX
+#define PEG_COMBINE_UMAX 2  // most vectors per lane per pass in the combine
+#endif
+#ifndef PEG_WGRAD_UMAX
+#define PEG_WGRAD_UMAX 2  // most vectors per lane per pass in wgrad
+#endif
+
+// Vectors per lane per pass: 1, 2 or 4, capped.
+static int pass_vectors(int64_t slice, int cap) {
+    const int u = lanes_per_pass(slice);
+    return u < cap ? u : cap;
+}
 
 template <int DT, int VEC>
 static peg_status combine_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
-                              int64_t q, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
+                              int64_t q, int64_t T, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra,
+                              int32_t E) {
     if (u == 1)
-        return launch(combine_kernel<DT, VEC, 1>, grid, dim3(kBlock), 0, s, y, out, nch, q, K, slot_row, w,
-                      ra.static_rows, ra.padded_bins, E);
-    return launch(combine_kernel<DT, VEC, 2>, grid, dim3(kBlock), 0, s, y, out, nch, q, K, slot_row, w,
-                  ra.static_rows, ra.padded_bins, E);
+        return launch(combine_kernel<DT, VEC, 1, PEG_COMBINE_WPT>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K,
+                      slot_row, w, ra.static_rows, ra.padded_bins, E);
+    if (u == 2)
+        return launch(combine_kernel<DT, VEC, 2, PEG_COMBINE_WPT>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K,
+                      slot_row, w, ra.static_rows, ra.padded_bins, E);
+#if PEG_COMBINE_UMAX >= 4
+    return launch(combine_kernel<DT, VEC, 4, PEG_COMBINE_WPT>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K,
+                  slot_row, w, ra.static_rows, ra.padded_bins, E);
+#else
+    return PEG_ERR_LAUNCH;
+#endif
 }
 
 template <int DT>
-static peg_status combine_dispatch(int vec, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
+static peg_status combine_dispatch(int vec, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch, int64_t T,
                                    int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
-    const int64_t q = wave_quarter(nch);
-    const int u = pass_vectors(q);
+    const int64_t q = wave_slice(nch, PEG_COMBINE_WPT);
+    const int u = pass_vectors(q, PEG_COMBINE_UMAX);
+    const dim3 grid((unsigned)token_blocks(T, PEG_COMBINE_WPT));
     switch (vec) {
-        case 16: return combine_vec<DT, 16>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
-        case 8: return combine_vec<DT, 8>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
-        case 4: return combine_vec<DT, 4>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
+        case 16: return combine_vec<DT, 16>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+        case 8: return combine_vec<DT, 8>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+        case 4: return combine_vec<DT, 4>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
         default:
-            if constexpr (Elem<DT>::bytes == 2) return combine_vec<DT, 2>(u, grid, s, y, out, nch, q, K, slot_row, w, ra, E);
+            if constexpr (Elem<DT>::bytes == 2)
+                return combine_vec<DT, 2>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
             return PEG_ERR_ALIGNMENT;
     }
 }
 
 template <int DT, int VEC>
 static peg_status wgrad_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg,
-                            int64_t nch, int64_t q, int32_t K, const int32_t* slot_row, RowArgs ra, int32_t E) {
+                            int64_t nch, int64_t q, int64_t T, int32_t K, const int32_t* slot_row, RowArgs ra,
+                            int32_t E) {
     if (u == 1)
-        return launch(wgrad_kernel<DT, VEC, 1>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, K, slot_row,
-                      ra.static_rows, ra.padded_bins, E);
-    return launch(wgrad_kernel<DT, VEC, 2>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, K, slot_row,
-                  ra.static_rows, ra.padded_bins, E);
+        return launch(wgrad_kernel<DT, VEC, 1, PEG_WGRAD_WPT>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, T, K,
+                      slot_row, ra.static_rows, ra.padded_bins, E);
+    if (u == 2)
+        return launch(wgrad_kernel<DT, VEC, 2, PEG_WGRAD_WPT>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, T, K,
+                      slot_row, ra.static_rows, ra.padded_bins, E);
+#if PEG_WGRAD_UMAX >= 4
+    return launch(wgrad_kernel<DT, VEC, 4, PEG_WGRAD_WPT>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, T, K,
+                  slot_row, ra.static_rows, ra.padded_bins, E);
+#else
+    return PEG_ERR_LAUNCH;
+#endif
 }
 
 template <int DT>
-static peg_status wgrad_dispatch(int vec, dim3 grid, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg,
-                                 int64_t nch, int32_t K, const int32_t* slot_row, RowArgs ra, int32_t E) {
-    const int64_t q = wave_quarter(nch);
-    const int u = pass_vectors(q);
+static peg_status wgrad_dispatch(int vec, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg, int64_t nch,
+                                 int64_t T, int32_t K, const int32_t* slot_row, RowArgs ra, int32_t E) {
+    const int64_t q = wave_slice(nch, PEG_WGRAD_WPT);
+    const int u = pass_vectors(q, PEG_WGRAD_UMAX);
+    const dim3 grid((unsigned)token_blocks(T, PEG_WGRAD_WPT));
     switch (vec) {
-        case 16: return wgrad_vec<DT, 16>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
-        case 8: return wgrad_vec<DT, 8>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
-        case 4: return wgrad_vec<DT, 4>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
+        case 16: return wgrad_vec<DT, 16>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
+        case 8: return wgrad_vec<DT, 8>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
+        case 4: return wgrad_vec<DT, 4>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
         default:
-            if constexpr (Elem<DT>::bytes == 2) return wgrad_vec<DT, 2>(u, grid, s, y, g, wg, nch, q, K, slot_row, ra, E);
+            if constexpr (Elem<DT>::bytes == 2)
+                return wgrad_vec<DT, 2>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
             return PEG_ERR_ALIGNMENT;
     }
 }
@@ -323,12 +361,11 @@ PEG_API peg_status peg_scatter_combine(const void* y, int32_t dtype, int32_t lay
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const dim3 grid((unsigned)T);
     const uint8_t* yb = (const uint8_t*)y;
     uint8_t* ob = (uint8_t*)out;
-    if (dtype == PEG_F32) return combine_dispatch<PEG_F32>(vec, grid, s, yb, ob, nch, K, slot_row, weights, ra, E);
-    if (dtype == PEG_BF16) return combine_dispatch<PEG_BF16>(vec, grid, s, yb, ob, nch, K, slot_row, weights, ra, E);
-    return combine_dispatch<PEG_F16>(vec, grid, s, yb, ob, nch, K, slot_row, weights, ra, E);
+    if (dtype == PEG_F32) return combine_dispatch<PEG_F32>(vec, s, yb, ob, nch, T, K, slot_row, weights, ra, E);
+    if (dtype == PEG_BF16) return combine_dispatch<PEG_BF16>(vec, s, yb, ob, nch, T, K, slot_row, weights, ra, E);
+    return combine_dispatch<PEG_F16>(vec, s, yb, ob, nch, T, K, slot_row, weights, ra, E);
 }
 
 PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int32_t layout, int64_t T, int64_t H,
@@ -346,10 +383,9 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const dim3 grid((unsigned)T);
     const uint8_t* yb = (const uint8_t*)y;
     const uint8_t* gb = (const uint8_t*)grad;
-    if (dtype == PEG_F32) return wgrad_dispatch<PEG_F32>(vec, grid, s, yb, gb, wgrad, nch, K, slot_row, ra, E);
-    if (dtype == PEG_BF16) return wgrad_dispatch<PEG_BF16>(vec, grid, s, yb, gb, wgrad, nch, K, slot_row, ra, E);
-    return wgrad_dispatch<PEG_F16>(vec, grid, s, yb, gb, wgrad, nch, K, slot_row, ra, E);
+    if (dtype == PEG_F32) return wgrad_dispatch<PEG_F32>(vec, s, yb, gb, wgrad, nch, T, K, slot_row, ra, E);
+    if (dtype == PEG_BF16) return wgrad_dispatch<PEG_BF16>(vec, s, yb, gb, wgrad, nch, T, K, slot_row, ra, E);
+    return wgrad_dispatch<PEG_F16>(vec, s, yb, gb, wgrad, nch, T, K, slot_row, ra, E);
 }

@@ -8,10 +8,10 @@
 // into its row; every other row of the tensor is zero.
 //
 // How (MI355X design, not the pages' Ascend sub-block buffering):
-//   * token-major: one block per token reads the token row once from HBM
-//     into VGPRs (16-byte lanes) and stores it to each of its <= K rows, so
-//     the source is read exactly once however many experts it goes to; each
-//     of the 4 waves owns a contiguous quarter of the row;
+//   * token-major: the waves of a token read its row once from HBM into
+//     VGPRs (16-byte lanes) and store it to each of its <= K rows, so the
+//     source is read exactly once however many experts it goes to; each wave
+//     owns a contiguous slice of the row;
 //   * the rows of a token come from the assignment -> row map (slot_row) by
 //     wave-uniform scalar loads, so the row loads issue at once, with no LDS
 //     staging or barrier in front of them;
@@ -23,24 +23,35 @@
 
 namespace peg {
 
-// Columns of a token row are split into 4 contiguous quarters, one per wave
-// of the block; a wave moves its quarter in passes of 64 lanes x U vectors.
-template <int VEC, int U>
+// Launch-shape knobs (build-time; defaults measured on MI355X).
+#ifndef PEG_GAP_UNITS
+#define PEG_GAP_UNITS 8192  // target vectors zeroed per gap block
+#endif
+#ifndef PEG_GAP_MAX
+#define PEG_GAP_MAX 2048  // most gap blocks per launch
+#endif
+constexpr int kZeroUnroll = 4;
+
+// The columns of a token row are split into WPT contiguous slices, one per
+// wave; a wave moves its slice in passes of 64 lanes x U vectors.
+template <int VEC, int U, int WPT>
 __global__ __launch_bounds__(kBlock) void gather_kernel(
-    const uint8_t* __restrict__ x, uint8_t* __restrict__ out, int64_t nch, int64_t quarter, int32_t K,
+    const uint8_t* __restrict__ x, uint8_t* __restrict__ out, int64_t nch, int64_t slice, int32_t K,
     const int32_t* __restrict__ slot_row, int64_t out_rows, int32_t layout, int32_t E, int32_t capacity,
-    const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int64_t token_blocks,
+    const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int64_t T, int64_t token_blocks,
     uint32_t* __restrict__ err_flag) {
     using V = typename VecOf<VEC>::T;
     const int64_t row_bytes = nch * VEC;
 
     if ((int64_t)blockIdx.x < token_blocks) {
         // ---------------- token row -> its expert rows ----------------
-        const int64_t t = blockIdx.x;
+        // (no barrier in this part: waves run independently)
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        const int64_t t = (int64_t)blockIdx.x * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+        if (t >= T) return;
         const int lane = lane_id();
-        const int64_t c_begin = w * quarter;
-        const int64_t c_end = c_begin + quarter < nch ? c_begin + quarter : nch;
+        const int64_t c_begin = (w % WPT) * slice;
+        const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
         const int32_t* my_rows = slot_row + t * K;
         // rows of the token: wave-uniform loads (scalar unit), K <= 8 kept in SGPRs
         int r8[kRowsFast];
@@ -57,7 +68,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
             if (r >= out_rows) over = true;
             any |= r >= 0 && r < out_rows;
         }
-        if (over && err_flag && threadIdx.x == 0) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
+        if (over && err_flag && lane == 0 && w % WPT == 0) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
         if (!any) return;  // token fully dropped: its row is never read
         const uint8_t* src = x + t * row_bytes;
         for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
@@ -129,50 +140,58 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
         carry += total;
     }
     if (threadIdx.x == 0) gpre[E] = carry;
-    __syncthreads();
+    lds_barrier();
 
     const int64_t units = (int64_t)carry * nch;
     const int64_t nz = (int64_t)gridDim.x - token_blocks;
     const int64_t zb = (int64_t)blockIdx.x - token_blocks;
     const int64_t lo = units * zb / nz;
     const int64_t hi = units * (zb + 1) / nz;
-    int64_t u = lo + threadIdx.x;
-    if (u >= hi) return;
-    // expert holding unit u: last e with gpre[e] * nch <= u
+    if (lo >= hi) return;
+    // first expert whose gap holds unit lo: last e with gpre[e] * nch <= lo
     int a = 0, b = E - 1;
     while (a < b) {
         const int mid = (a + b + 1) >> 1;
-        if ((int64_t)gpre[mid] * nch <= u) a = mid;
+        if ((int64_t)gpre[mid] * nch <= lo) a = mid;
         else b = mid - 1;
     }
-    int e = a;
+    // walk this block's range one expert gap (a contiguous byte range) at a
+    // time, kZeroUnroll stores in flight per thread
     const V z = zero_vec<VEC>();
-    for (; u < hi; u += kBlock) {
-        while ((int64_t)gpre[e + 1] * nch <= u) ++e;
-        const int64_t dst_unit = (int64_t)gstart[e] * nch + (u - (int64_t)gpre[e] * nch);
-        stream_store<VEC>(out, dst_unit, z);
+    int64_t u0 = lo;
+    for (int e = a; u0 < hi && e < E; ++e) {
+        const int64_t seg_end = (int64_t)gpre[e + 1] * nch < hi ? (int64_t)gpre[e + 1] * nch : hi;
+        const int64_t shift = (int64_t)gstart[e] * nch - (int64_t)gpre[e] * nch;  // unit -> output vector
+        for (int64_t u = u0 + threadIdx.x; u < seg_end; u += (int64_t)kBlock * kZeroUnroll) {
+#pragma unroll
+            for (int j = 0; j < kZeroUnroll; ++j) {
+                const int64_t uu = u + (int64_t)j * kBlock;
+                if (uu < seg_end) stream_store<VEC>(out, shift + uu, z);
+            }
+        }
+        u0 = seg_end > u0 ? seg_end : u0;
     }
 }
 
 struct GatherArgs {
     const uint8_t* x;
     uint8_t* out;
-    int64_t nch, quarter;
+    int64_t nch, slice;
     int32_t K;
     const int32_t* slot_row;
     int64_t out_rows;
     int32_t layout, E, capacity;
     const int32_t* bins;
     const int32_t* padded_bins;
-    int64_t token_blocks;
+    int64_t T, token_blocks;
     uint32_t* err_flag;
 };
 
-template <int VEC>
+template <int VEC, int WPT>
 static peg_status gather_launch(int u, dim3 grid, hipStream_t s, const GatherArgs& a) {
 #define PEG_GATHER_U(UU)                                                                                        \
-    return launch(gather_kernel<VEC, UU>, grid, dim3(kBlock), 0, s, a.x, a.out, a.nch, a.quarter, a.K,        \
-                  a.slot_row, a.out_rows, a.layout, a.E, a.capacity, a.bins, a.padded_bins, a.token_blocks,    \
+    return launch(gather_kernel<VEC, UU, WPT>, grid, dim3(kBlock), 0, s, a.x, a.out, a.nch, a.slice, a.K,   \
+                  a.slot_row, a.out_rows, a.layout, a.E, a.capacity, a.bins, a.padded_bins, a.T, a.token_blocks, \
                   a.err_flag)
     if (u == 1) PEG_GATHER_U(1);
     if (u == 2) PEG_GATHER_U(2);
@@ -183,10 +202,10 @@ static peg_status gather_launch(int u, dim3 grid, hipStream_t s, const GatherArg
 // Zero-fill blocks: enough that each writes a few hundred KB at most.
 static int64_t gap_blocks(int64_t max_gap_rows, int64_t nch, int vec) {
     const int64_t units = max_gap_rows * nch;
-    int64_t b = (units + 4096 - 1) / 4096;
+    int64_t b = (units + PEG_GAP_UNITS - 1) / PEG_GAP_UNITS;
     (void)vec;
     if (b < 1) b = 1;
-    if (b > 2048) b = 2048;
+    if (b > PEG_GAP_MAX) b = PEG_GAP_MAX;
     return b;
 }
 
@@ -218,16 +237,26 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
     }
     const int64_t nch = row_bytes / vec;
     const int64_t nz = gap_blocks(out_rows, nch, vec);
-    const dim3 grid((unsigned)(T + nz));
-    const int64_t quarter = wave_quarter(nch);
-    const int u = lanes_per_pass(quarter);
-    const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, quarter, K, slot_row, out_rows, layout, E, capacity,
-                       bins, padded_bins, T, err_flag};
+    const int wpt = gather_wpt(nch);
+    const int64_t tb = token_blocks(T, wpt);
+    const dim3 grid((unsigned)(tb + nz));
+    const int64_t slice = wave_slice(nch, wpt);
+    const int u = lanes_per_pass(slice);
+    const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, slice, K, slot_row, out_rows, layout, E, capacity,
+                       bins, padded_bins, T, tb, err_flag};
+    if (wpt == 2) {
+        switch (vec) {
+            case 16: return gather_launch<16, 2>(u, grid, s, a);
+            case 8: return gather_launch<8, 2>(u, grid, s, a);
+            case 4: return gather_launch<4, 2>(u, grid, s, a);
+            default: return gather_launch<2, 2>(u, grid, s, a);
+        }
+    }
     switch (vec) {
-        case 16: return gather_launch<16>(u, grid, s, a);
-        case 8: return gather_launch<8>(u, grid, s, a);
-        case 4: return gather_launch<4>(u, grid, s, a);
-        default: return gather_launch<2>(u, grid, s, a);
+        case 16: return gather_launch<16, 4>(u, grid, s, a);
+        case 8: return gather_launch<8, 4>(u, grid, s, a);
+        case 4: return gather_launch<4, 4>(u, grid, s, a);
+        default: return gather_launch<2, 4>(u, grid, s, a);
     }
 }
 

@@ -178,6 +178,21 @@ struct Lanes {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Block barrier that orders LDS accesses only: global stores issued before it
+// stay in flight (__syncthreads would wait for them to complete). For
+// barriers that protect LDS data; global data shared between the threads of
+// a block still needs __syncthreads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// popcount(mask & lanes below this one), in two instructions.
+__device__ __forceinline__ int rank_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 __device__ __forceinline__ uint64_t lanes_below() {
     return (uint64_t(1) << lane_id()) - 1;  // lane 0 -> 0
 }
@@ -209,16 +224,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     const int w = threadIdx.x / kWave;
     int inc = wave_inclusive_scan(v);
     if (lane == kWave - 1) scratch[w] = inc;
-    __syncthreads();
+    lds_barrier();
     if (w == 0) {
         int t = lane < NW ? scratch[lane] : 0;
         t = wave_inclusive_scan(t);
         if (lane < NW) scratch[lane] = t;
     }
-    __syncthreads();
+    lds_barrier();
     int prefix = (w ? scratch[w - 1] : 0) + inc - v;
     *total = scratch[NW - 1];
-    __syncthreads();
+    lds_barrier();
     return prefix;
 }
 

@@ -35,25 +35,52 @@ inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, con
     return 0;
 }
 
-// A row of nch vectors is split over the 4 waves of a block: each wave owns
-// a contiguous quarter, rounded up to 8 vectors (128 bytes at 16-byte
+// The token kernels give each token WPT waves (4, 2 or 1) of a 4-wave
+// block, so a block holds 4 / WPT tokens. Measured on MI355X: the gather
+// likes 2 waves per token for rows of at most 512 vectors and 4 above, the
+// combine 4, the wgrad 2.
+#ifndef PEG_COMBINE_WPT
+#define PEG_COMBINE_WPT 4
+#endif
+#ifndef PEG_WGRAD_WPT
+#define PEG_WGRAD_WPT 2
+#endif
+#ifndef PEG_GATHER_WPT_SPLIT
+#define PEG_GATHER_WPT_SPLIT 512  // rows of at most this many vectors: 2 waves per token
+#endif
+
+inline int gather_wpt(int64_t nch) { return nch <= PEG_GATHER_WPT_SPLIT ? 2 : 4; }
+
+template <int WPT>
+struct TokenMap {
+    static_assert(WPT == 1 || WPT == 2 || WPT == 4, "waves per token must be 1, 2 or 4");
+    static constexpr int kTokensPerBlock = (kBlock / 64) / WPT;
+};
+
+// A row of nch vectors is split over the wpt waves of its token: each wave
+// owns a contiguous slice, rounded up to 8 vectors (128 bytes at 16-byte
 // vectors) so that every wave starts on a cache-line boundary.
-inline int64_t wave_quarter(int64_t nch) {
-    const int64_t q = (nch + 3) / 4;
+inline int64_t wave_slice(int64_t nch, int wpt) {
+    const int64_t q = (nch + wpt - 1) / wpt;
     return (q + 7) & ~int64_t(7);
 }
 
-// Vectors per lane per pass (1, 2 or 4) so that one pass covers a quarter
+// Vectors per lane per pass (1, 2 or 4) so that one pass covers a slice
 // when it can.
-inline int lanes_per_pass(int64_t quarter) {
-    const int64_t p = (quarter + 63) / 64;
+inline int lanes_per_pass(int64_t slice) {
+    const int64_t p = (slice + 63) / 64;
     return p <= 1 ? 1 : (p <= 2 ? 2 : 4);
+}
+
+inline int64_t token_blocks(int64_t T, int wpt) {
+    const int64_t per = (kBlock / 64) / wpt;
+    return (T + per - 1) / per;
 }
 
 // Tiles of the routing preparation: 256 threads x ITEMS assignments. The
 // per-chunk count table of a tile (4 * ITEMS chunks of 64 x E ints) stays
 // within 32 KB of LDS.
-inline int prep_items(int32_t E) { return E <= 256 ? 8 : (E <= 512 ? 4 : 2); }
+inline int prep_items(int32_t E) { return E <= 128 ? 16 : (E <= 256 ? 8 : (E <= 512 ? 4 : 2)); }
 inline int64_t prep_tile(int32_t E) { return (int64_t)kBlock * prep_items(E); }
 inline int64_t prep_tiles(int64_t total, int32_t E) { return (total + prep_tile(E) - 1) / prep_tile(E); }
 

@@ -11,52 +11,71 @@
 // Ranking inside a 64-id chunk is a wave64 "multisplit": ballots over the bits
 // of the expert id give every lane the mask of lanes holding the same expert;
 // its rank is the popcount of that mask below the lane. Per-(chunk, expert)
-// counts are then scanned over chunks in LDS (one wave64 scan per expert),
-// which keeps ascending assignment id inside every expert (a stable sort).
-// No global atomics; the result is deterministic.
+// counts are then scanned over chunks in LDS, which keeps ascending
+// assignment id inside every expert (a stable sort). No global atomics; the
+// result is deterministic.
 //
-// Two paths:
+// Paths:
 //   small: T*K <= 16384 and its count table fits in LDS -> one 1024-thread
 //          block does everything (histogram, scans, placement) in one launch;
-//   tiled: tiles of 256*ITEMS ids; three launches (tile histograms, one
-//          expert-major scan that yields each (expert, tile) base position
-//          and the bins, placement).
+//   tiled: tiles of 256*ITEMS ids; a histogram launch, then a placement
+//          launch in which every block reads the (experts x tiles) count
+//          table and derives its own bases (block 0 also writes the bins);
+//          when that table is large, a single-block scan launch in between
+//          computes the bases once.
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
 namespace peg {
 
-// Mask of the lanes of this wave whose expert id equals this lane's.
-__device__ __forceinline__ uint64_t same_expert_mask(int v, bool valid, int nbits) {
-    uint64_t same = __ballot(valid);
+// Mask of the lanes of this wave whose expert id equals this lane's (0 for
+// a lane without a valid id): one ballot per bit of the id; a lane keeps the
+// lanes that agree with it on every bit.
+__device__ __forceinline__ uint64_t same_expert_mask(int v, bool valid, int nbits, int /*E*/) {
+    uint64_t same = __builtin_amdgcn_ballot_w64(valid);
     for (int b = 0; b < nbits; ++b) {
         const bool bit = (v >> b) & 1;
-        const uint64_t ones = __ballot(valid && bit);
+        const uint64_t ones = __builtin_amdgcn_ballot_w64(bit);
         same &= bit ? ones : ~ones;
     }
-    return same;
+    return valid ? same : 0;
 }
 
-// In-place exclusive scan over the NCH chunks of every expert column of the
-// LDS table cnt[NCH][E]; one wave per expert (waves stride over experts),
-// 64 chunks per pass. tot[e] (optional) receives each expert's total.
-// Must be called by the whole block; ends with a barrier.
-template <int NW>
+// In-place exclusive scan over the nch chunks of every expert column of the
+// LDS table cnt[nch][E]; tot[e] (optional) receives each expert's total.
+// Few experts: one wave per expert, a wave64 scan per 64 chunks. Many
+// experts: one thread per expert walks its column (conflict-free: adjacent
+// threads read adjacent words). Must be called by the whole block; ends
+// with a barrier.
+template <int NT>
 __device__ __forceinline__ void scan_chunks(int* cnt, int nch, int E, int* tot) {
-    const int lane = lane_id();
-    const int w = threadIdx.x / kWave;
-    for (int e = w; e < E; e += NW) {
-        int carry = 0;
-        for (int c0 = 0; c0 < nch; c0 += kWave) {
-            const int c = c0 + lane;
-            const int v = c < nch ? cnt[c * E + e] : 0;
-            const int inc = wave_inclusive_scan(v);
-            if (c < nch) cnt[c * E + e] = carry + inc - v;
-            carry += __shfl(inc, kWave - 1, kWave);
+    constexpr int NW = NT / kWave;
+    if (E <= 16 * NW) {
+        const int lane = lane_id();
+        const int w = threadIdx.x / kWave;
+        for (int e = w; e < E; e += NW) {
+            int carry = 0;
+            for (int c0 = 0; c0 < nch; c0 += kWave) {
+                const int c = c0 + lane;
+                const int v = c < nch ? cnt[c * E + e] : 0;
+                const int inc = wave_inclusive_scan(v);
+                if (c < nch) cnt[c * E + e] = carry + inc - v;
+                carry += __shfl(inc, kWave - 1, kWave);
+            }
+            if (tot && lane == 0) tot[e] = carry;
         }
-        if (tot && lane == 0) tot[e] = carry;
+    } else {
+        for (int e = threadIdx.x; e < E; e += NT) {
+            int run = 0;
+            for (int c = 0; c < nch; ++c) {
+                const int v = cnt[c * E + e];
+                cnt[c * E + e] = run;
+                run += v;
+            }
+            if (tot) tot[e] = run;
+        }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Row of sorted position pos of expert e ([BIN]/[PAD] Implementation Pattern).
@@ -72,8 +91,52 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int64_t kSmallMaxIds = 16384;
 constexpr size_t kSmallMaxTable = 48 * 1024;
+constexpr size_t kSmallMaxLds = 64 * 1024 - 512;  // dynamic LDS budget of the small path
 
-template <int ITEMS>
+// Exclusive scan over experts of `count` (LDS, E <= 1024 entries) by wave 0
+// alone: each lane sums a run of consecutive experts, one wave64 scan, then
+// the run prefixes. Writes start[e] (and padded starts / bins when asked);
+// returns the total through *n_out. Call from wave 0 only.
+__device__ __forceinline__ void wave0_bins(const int* count, int E, int pad_multiple, int* start, int* pstart,
+                                           int32_t* bins, int32_t* padded_bins, int32_t* tokens_per_expert,
+                                           int* n_out) {
+    const int lane = lane_id();
+    const int per = (E + kWave - 1) / kWave;  // experts per lane
+    const int e0 = lane * per;
+    int run = 0, prun = 0;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            run += count[e];
+            if (padded_bins) prun += ((count[e] + pad_multiple - 1) / pad_multiple) * pad_multiple;
+        }
+    }
+    const int inc = wave_inclusive_scan(run);
+    const int pinc = wave_inclusive_scan(prun);
+    int pre = inc - run, ppre = pinc - prun;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            const int c = count[e];
+            start[e] = pre;
+            bins[e] = pre + c;
+            if (tokens_per_expert) tokens_per_expert[e] = c;
+            pre += c;
+            if (padded_bins) {
+                const int r = ((c + pad_multiple - 1) / pad_multiple) * pad_multiple;
+                pstart[e] = ppre;
+                padded_bins[e] = ppre + r;
+                ppre += r;
+            }
+        }
+    }
+    if (lane == kWave - 1) *n_out = inc;
+}
+
+// STAGE: indices are first scattered into LDS by sorted position, then
+// indices and bin_ids are written out with consecutive threads on
+// consecutive positions (coalesced), instead of one scattered store per id.
+template <int ITEMS, bool STAGE>
 __global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
     const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, int32_t pad_multiple, int32_t layout,
     int32_t capacity, int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
@@ -85,7 +148,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
     int* start = cnt + NCH * E;     // [E] first sorted position of each expert
     int* pstart = start + E;        // [E] first padded row of each expert
     int* tot = pstart + E;          // [E] count of each expert
-    __shared__ int scratch[kSmallWaves];
+    int* sidx = tot + E;            // [total] assignment id by sorted position (STAGE)
     __shared__ int s_n;
 
     // ids first: their loads overlap the table clearing
@@ -96,44 +159,22 @@ __global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
         v[j] = a < total ? top[a] : -1;
     }
     for (int i = threadIdx.x; i < NCH * E; i += kSmallThreads) cnt[i] = 0;
-    __syncthreads();
+    lds_barrier();
 
     const int w = threadIdx.x / kWave;
     int rank[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const bool valid = (unsigned)v[j] < (unsigned)E;
-        const uint64_t same = same_expert_mask(v[j], valid, nbits);
-        rank[j] = __popcll(same & lanes_below());
+        const uint64_t same = same_expert_mask(v[j], valid, nbits, E);
+        rank[j] = rank_below(same);
         if (valid && rank[j] == 0) cnt[(j * kSmallWaves + w) * E + v[j]] = __popcll(same);
         if (!valid) v[j] = -1;
     }
-    __syncthreads();
-    scan_chunks<kSmallWaves>(cnt, NCH, E, tot);
-
-    // bins: inclusive scan of the counts over experts (E <= 1024 = threads)
-    {
-        const int e = threadIdx.x;
-        const int count = e < E ? tot[e] : 0;
-        int n;
-        const int pre = block_exclusive_scan<kSmallThreads>(count, scratch, &n);
-        if (e < E) {
-            start[e] = pre;
-            bins[e] = pre + count;
-            if (tokens_per_expert) tokens_per_expert[e] = count;
-        }
-        if (e == 0) s_n = n;
-        if (padded_bins) {
-            const int rounded = e < E ? ((count + pad_multiple - 1) / pad_multiple) * pad_multiple : 0;
-            int ptotal;
-            const int ppre = block_exclusive_scan<kSmallThreads>(rounded, scratch, &ptotal);
-            if (e < E) {
-                pstart[e] = ppre;
-                padded_bins[e] = ppre + rounded;
-            }
-        }
-    }
-    __syncthreads();
+    lds_barrier();
+    scan_chunks<kSmallThreads>(cnt, NCH, E, tot);  // ends with a barrier
+    if (w == 0) wave0_bins(tot, E, pad_multiple, start, pstart, bins, padded_bins, tokens_per_expert, &s_n);
+    lds_barrier();
 
     const int n = s_n;
 #pragma unroll
@@ -143,16 +184,36 @@ __global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
         const int e = v[j];
         if (e >= 0) {
             const int pos = start[e] + cnt[(j * kSmallWaves + w) * E + e] + rank[j];
-            indices[pos] = (int32_t)a;
-            bin_ids[pos] = e;
+            if constexpr (STAGE) {
+                sidx[pos] = (int)a;
+            } else {
+                indices[pos] = (int32_t)a;
+                bin_ids[pos] = e;
+            }
             if (slot_row)
                 slot_row[a] = position_row(layout, e, capacity, pos - start[e], padded_bins ? pstart[e] : 0);
         } else if (slot_row) {
             slot_row[a] = -1;
         }
-        if (a >= n) {
-            indices[a] = -1;
-            bin_ids[a] = -1;
+        if constexpr (!STAGE) {
+            if (a >= n) {
+                indices[a] = -1;
+                bin_ids[a] = -1;
+            }
+        }
+    }
+    if constexpr (STAGE) {
+        lds_barrier();  // the slot_row stores above stay in flight
+        int e = 0;  // expert of position p: positions rise with p, so e only moves forward
+        for (int64_t p = threadIdx.x; p < total; p += kSmallThreads) {
+            if (p < n) {
+                while (e + 1 < E && start[e + 1] <= p) ++e;
+                indices[p] = sidx[p];
+                bin_ids[p] = e;
+            } else {
+                indices[p] = -1;
+                bin_ids[p] = -1;
+            }
         }
     }
 }
@@ -174,11 +235,11 @@ __global__ __launch_bounds__(kBlock) void tile_hist_kernel(const int32_t* __rest
         v[j] = a < total ? top[a] : -1;
     }
     for (int e = threadIdx.x; e < E; e += kBlock) hist[e] = 0;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
         if ((unsigned)v[j] < (unsigned)E) atomicAdd(&hist[v[j]], 1);
-    __syncthreads();
+    lds_barrier();
     for (int e = threadIdx.x; e < E; e += kBlock) counts[(int64_t)e * ntiles + blockIdx.x] = hist[e];
 }
 
@@ -235,11 +296,18 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
     }
 }
 
+// Placement of one tile. With bases_ready (after tile_scan_kernel), `counts`
+// holds the first sorted position of every (expert, tile) and bins /
+// padded_bins are final. Otherwise `counts` holds the tile histograms and
+// every block derives its own bases from them (the whole table is small:
+// at most kMergedMaxTable ints); block 0 also writes tokens_per_expert,
+// bins and padded_bins.
 template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void tile_place_kernel(
-    const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, const int32_t* __restrict__ base_pos,
-    int64_t ntiles, const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int32_t layout,
-    int32_t capacity, int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids, int32_t* __restrict__ slot_row) {
+    const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, const int32_t* __restrict__ counts,
+    int64_t ntiles, int32_t bases_ready, int32_t pad_multiple, int32_t layout, int32_t capacity,
+    int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids, int32_t* __restrict__ tokens_per_expert,
+    int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins, int32_t* __restrict__ slot_row) {
     constexpr int NW = kBlock / kWave;
     constexpr int NCH = ITEMS * NW;  // 64-id chunks per tile
     extern __shared__ int lds[];
@@ -247,6 +315,7 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
     int* tbase = cnt + NCH * E;  // [E] first sorted position of (e, this tile)
     int* start = tbase + E;      // [E] first sorted position of e
     int* pstart = start + E;     // [E] first padded row of e
+    __shared__ int scratch[NW];
     __shared__ int s_n;
 
     const int64_t base = (int64_t)blockIdx.x * (kBlock * ITEMS);
@@ -256,27 +325,63 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
         const int64_t a = base + j * kBlock + threadIdx.x;
         v[j] = a < total ? top[a] : -1;
     }
-    for (int e = threadIdx.x; e < E; e += kBlock) {
-        tbase[e] = base_pos[(int64_t)e * ntiles + blockIdx.x];
-        start[e] = e ? bins[e - 1] : 0;
-        pstart[e] = (padded_bins && e) ? padded_bins[e - 1] : 0;
+    if (bases_ready) {
+        for (int e = threadIdx.x; e < E; e += kBlock) {
+            start[e] = e ? bins[e - 1] : 0;
+            tbase[e] = counts[(int64_t)e * ntiles + blockIdx.x];
+            pstart[e] = (padded_bins && e) ? padded_bins[e - 1] : 0;
+        }
+        if (threadIdx.x == 0) s_n = bins[E - 1];
+    } else {
+        // this tile's offset inside each expert, each expert's total, then
+        // scans over the experts for the starts
+        int carry = 0, pcarry = 0;
+        for (int e0 = 0; e0 < E; e0 += kBlock) {
+            const int e = e0 + threadIdx.x;
+            int before = 0, count = 0;
+            if (e < E) {
+                const int32_t* row = counts + (int64_t)e * ntiles;
+                for (int64_t t = 0; t < ntiles; ++t) {
+                    const int c = row[t];
+                    before += t < (int64_t)blockIdx.x ? c : 0;
+                    count += c;
+                }
+            }
+            int sum;
+            const int pre = carry + block_exclusive_scan<kBlock>(count, scratch, &sum);
+            carry += sum;
+            const int rounded = padded_bins ? ((count + pad_multiple - 1) / pad_multiple) * pad_multiple : 0;
+            int psum;
+            const int ppre = pcarry + block_exclusive_scan<kBlock>(rounded, scratch, &psum);
+            pcarry += psum;
+            if (e < E) {
+                start[e] = pre;
+                tbase[e] = pre + before;
+                pstart[e] = ppre;
+                if (blockIdx.x == 0) {
+                    bins[e] = pre + count;
+                    if (tokens_per_expert) tokens_per_expert[e] = count;
+                    if (padded_bins) padded_bins[e] = ppre + rounded;
+                }
+            }
+        }
+        if (threadIdx.x == 0) s_n = carry;
     }
-    if (threadIdx.x == 0) s_n = bins[E - 1];
     for (int i = threadIdx.x; i < NCH * E; i += kBlock) cnt[i] = 0;
-    __syncthreads();
+    lds_barrier();
 
     const int w = threadIdx.x / kWave;
     int rank[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const bool valid = (unsigned)v[j] < (unsigned)E;
-        const uint64_t same = same_expert_mask(v[j], valid, nbits);
-        rank[j] = __popcll(same & lanes_below());
+        const uint64_t same = same_expert_mask(v[j], valid, nbits, E);
+        rank[j] = rank_below(same);
         if (valid && rank[j] == 0) cnt[(j * NW + w) * E + v[j]] = __popcll(same);
         if (!valid) v[j] = -1;
     }
-    __syncthreads();
-    scan_chunks<NW>(cnt, NCH, E, nullptr);
+    lds_barrier();
+    scan_chunks<kBlock>(cnt, NCH, E, nullptr);
 
     const int n = s_n;
 #pragma unroll
@@ -305,26 +410,37 @@ static int id_bits(int E) {
     return nbits;
 }
 
+// Tiles whose histogram table (experts x tiles) is at most this many ints
+// skip the separate scan launch: each placement block reads the table.
+constexpr int64_t kMergedMaxTable = 16384;
+
 template <int ITEMS>
 static peg_status prep_tiled(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
                              int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
                              int32_t* padded_bins, int32_t* slot_row, int32_t* counts, hipStream_t s) {
-    const int64_t ntiles = prep_tiles(total, E);
+    const int64_t ntiles = (total + (int64_t)kBlock * ITEMS - 1) / ((int64_t)kBlock * ITEMS);
     PEG_CHECK(launch(tile_hist_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), 0, s, top, total, E, ntiles,
                      counts));
-    PEG_CHECK(launch(tile_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E, pad_multiple, tpe,
-                     bins, padded_bins));
+    const int32_t merged = ntiles * E <= kMergedMaxTable ? 1 : 0;
+    if (!merged || ntiles == 0)
+        PEG_CHECK(launch(tile_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E, pad_multiple, tpe,
+                         bins, padded_bins));
     const size_t lds = ((size_t)ITEMS * (kBlock / kWave) * E + 3 * (size_t)E) * sizeof(int);
     return launch(tile_place_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,
-                  id_bits(E), counts, ntiles, bins, padded_bins, layout, capacity, indices, bin_ids, slot_row);
+                  id_bits(E), counts, ntiles, merged ? 0 : 1, pad_multiple, layout, capacity, indices, bin_ids, tpe,
+                  bins, padded_bins, slot_row);
 }
 
 template <int ITEMS>
 static peg_status prep_small(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
                              int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
                              int32_t* padded_bins, int32_t* slot_row, hipStream_t s) {
-    const size_t lds = ((size_t)ITEMS * kSmallWaves * E + 3 * (size_t)E) * sizeof(int);
-    return launch(prep_small_kernel<ITEMS>, dim3(1), dim3(kSmallThreads), lds, s, top, total, E, id_bits(E),
+    const size_t base = ((size_t)ITEMS * kSmallWaves * E + 3 * (size_t)E) * sizeof(int);
+    const size_t staged = base + (size_t)total * sizeof(int);
+    if (staged <= kSmallMaxLds)
+        return launch(prep_small_kernel<ITEMS, true>, dim3(1), dim3(kSmallThreads), staged, s, top, total, E,
+                      id_bits(E), pad_multiple, layout, capacity, indices, bin_ids, tpe, bins, padded_bins, slot_row);
+    return launch(prep_small_kernel<ITEMS, false>, dim3(1), dim3(kSmallThreads), base, s, top, total, E, id_bits(E),
                   pad_multiple, layout, capacity, indices, bin_ids, tpe, bins, padded_bins, slot_row);
 }
 
@@ -374,6 +490,9 @@ PEG_API peg_status peg_route_prep(const int32_t* top_experts, int64_t T, int32_t
     }
     int32_t* counts = reinterpret_cast<int32_t*>(ws);
     const int items = prep_items(E);
+    if (items == 16)
+        return prep_tiled<16>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                              tokens_per_expert, bins, padded_bins, slot_row, counts, s);
     if (items == 8)
         return prep_tiled<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
                              tokens_per_expert, bins, padded_bins, slot_row, counts, s);
