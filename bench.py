@@ -40,13 +40,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash():
+KERNEL_SOURCES = {"gather": "gather.hip", "combine": "combine.hip", "wgrad": "combine.hip",
+                  "route_prep": "route_prep.hip", "compact": "compact.hip"}
+
+
+def source_hash(kernel=None):
+    """Hash of a kernel's source file and the shared headers (all sources when
+    kernel is None): counter data recorded for a kernel is used only while
+    this hash is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "padded_expert_gather_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc))
+    if kernel is not None:
+        names = [n for n in names if n.endswith(".hpp") or n == KERNEL_SOURCES[kernel]]
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
+    with open(os.path.join(ROOT, "include", "peg.h"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -260,7 +272,7 @@ def traffic_for(kernel, workload_name):
     with open(path) as f:
         d = json.load(f)
     e = d.get(workload_name, {}).get(kernel)
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -363,7 +375,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "source_hash": source_hash(),
+        "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},
     }
     print(json.dumps(line), flush=True)
 
