@@ -51,6 +51,9 @@ def load_library(path):
     lib.pego_wgrad.argtypes = [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_int32, c_int32,
                                c_int32, c_int32, i32p, i32p, i32p, i32p, i64p, c_int64, f32p, f64p]
     lib.pego_wgrad.restype = c_int32
+    lib.pego_combine_backward_dy.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, c_int32,
+                                             i32p, i32p, i32p, i32p, f32p, c_int64, i64p, c_int64, c_void_p]
+    lib.pego_combine_backward_dy.restype = c_int32
     lib.pego_routing_map_compact.argtypes = [c_void_p, c_int32, POINTER(c_uint8), c_int64, c_int32, c_int32,
                                              f32p, i32p]
     lib.pego_routing_map_compact.restype = c_int32
@@ -211,6 +214,27 @@ def wgrad(y, grad, dtype, r, layout, capacity=None, tokens=None, with_scale=Fals
     if rc != 0:
         raise ValueError("oracle wgrad refused its arguments")
     return (out, scale) if with_scale else out
+
+
+def combine_backward_dy(dout, dtype, r, layout, capacity=None, weights=None, rows=None, R=None):
+    """Gradient of the combine with respect to the expert tensor: kept row of
+    assignment a gets w[a] * dout[a // K] (raw copy without weights), other
+    rows 0. ``rows``: optional sample of expert-tensor rows."""
+    dout = np.ascontiguousarray(dout)
+    T, H = dout.shape
+    if R is None:
+        R = expert_rows(r, layout, capacity)
+    w = _c(weights, np.float32)
+    rows_arr = _c(rows, np.int64)
+    count = R if rows_arr is None else rows_arr.shape[0]
+    out = np.empty((count, H), dtype=dout.dtype)
+    rc = _load().pego_combine_backward_dy(_vp(dout), dtype, T, H, r.K, r.E, layout, capacity or 0,
+                                          _p(r.indices, c_int32), _p(r.bin_ids, c_int32), _p(r.bins, c_int32),
+                                          _p(r.padded_bins, c_int32), _p(w, c_float), R, _p(rows_arr, c_int64),
+                                          0 if rows_arr is None else count, _vp(out))
+    if rc != 0:
+        raise ValueError("oracle combine_backward_dy refused its arguments")
+    return out
 
 
 def routing_map_compact(probs, probs_dtype, routing_map, topk):

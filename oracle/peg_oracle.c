@@ -416,6 +416,63 @@ int pego_wgrad(const void* y, const void* grad, int32_t dtype, int64_t R, int64_
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the combine with respect to the expert tensor.               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The combine of [BIN] Workflow step 5 / [PAD] Workflow step 6 is linear in
+ * the expert tensor: out[t] = sum over kept k of w[t*K+k] * y[row(t*K+k)].
+ * Its gradient with respect to y, given the upstream gradient dout [T, H],
+ * is therefore: every kept sorted position i with assignment a = indices[i]
+ * gets w[a] * dout[a / K] in its row (the weighted gather of dout through
+ * the same mapping, "maps gradients through padded expert storage" in the
+ * [PAD] description); every other row of the R-row tensor is zero. Without
+ * weights (factor 1) the rows are copied as raw bits. The product runs in
+ * double and is rounded once to dtype. rows == NULL: dy holds all R rows;
+ * otherwise dy[j] is row rows[j] (a sample).
+ */
+int pego_combine_backward_dy(const void* dout, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
+                             int32_t layout, int32_t capacity, const int32_t* indices, const int32_t* bin_ids,
+                             const int32_t* bins, const int32_t* padded_bins, const float* weights, int64_t R,
+                             const int64_t* rows, int64_t nrows, void* dy) {
+    if (!dtype_ok(dtype) || T < 0 || H < 0 || K < 1 || E < 1 || R < 0 || !dout || !bins || !dy) return -1;
+    if (layout == PEGO_BINNED && capacity < 1) return -1;
+    if (layout == PEGO_PADDED && !padded_bins) return -1;
+    int64_t total = T * (int64_t)K;
+    /* assignment held by each row of the expert tensor; -1 = zero row */
+    int64_t* src = (int64_t*)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
+    if (!src) return -1;
+    for (int64_t r = 0; r < R; ++r) src[r] = -1;
+    int64_t n = valid_count(bins, E, total);
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t row = position_row(i, E, layout, capacity, bin_ids, bins, padded_bins);
+        if (row == -2) { free(src); return -1; }
+        if (row < 0 || row >= R) continue;
+        if (indices[i] < 0 || indices[i] >= total) { free(src); return -1; }
+        src[row] = indices[i];
+    }
+    int eb = dtype == PEGO_F32 ? 4 : 2;
+    int64_t count = rows ? nrows : R;
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t r = rows ? rows[j] : j;
+        int64_t a = (r >= 0 && r < R) ? src[r] : -1;
+        if (a < 0) {
+            memset((uint8_t*)dy + j * H * eb, 0, (size_t)(H * eb));
+            continue;
+        }
+        int64_t t = a / K;
+        if (!weights) {
+            memcpy((uint8_t*)dy + j * H * eb, (const uint8_t*)dout + t * H * eb, (size_t)(H * eb));
+            continue;
+        }
+        double w = (double)weights[a];
+        for (int64_t h = 0; h < H; ++h) pego_store(dy, dtype, j * H + h, w * pego_load(dout, dtype, t * H + h));
+    }
+    free(src);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Routing-map compaction.                                                  */
 /* ------------------------------------------------------------------------ */
 

@@ -61,6 +61,11 @@ int pego_wgrad(const void* y, const void* grad, int32_t dtype, int64_t R, int64_
                const int32_t* bin_ids, const int32_t* bins, const int32_t* padded_bins,
                const int64_t* tokens, int64_t ntok, float* wgrad, double* scale);
 
+int pego_combine_backward_dy(const void* dout, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
+                             int32_t layout, int32_t capacity, const int32_t* indices, const int32_t* bin_ids,
+                             const int32_t* bins, const int32_t* padded_bins, const float* weights, int64_t R,
+                             const int64_t* rows, int64_t nrows, void* dy);
+
 int pego_routing_map_compact(const void* probs, int32_t probs_dtype, const uint8_t* routing_map,
                              int64_t T, int32_t E, int32_t topk, float* probs_out,
                              int32_t* route_experts);

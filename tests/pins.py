@@ -453,6 +453,35 @@ def pin_sampled_tokens(o):
     assert np.array_equal(o.wgrad(y, grad, W.BF16, r, W.PADDED, tokens=tok), fw[tok])
 
 
+def pin_combine_backward(o):
+    """Gradient of the combine w.r.t. the expert tensor vs torch autograd of
+    the index_add combine (float64, rounded output within one ulp); rows that
+    hold no kept assignment get exactly 0; without weights it is the gather of
+    the upstream gradient, bit for bit; the row sample equals the full rows."""
+    import torch
+    rng = np.random.default_rng(81)
+    for top, w, E in _tiny_cases():
+        T, K = top.shape
+        for dtype in (W.F32, W.BF16):
+            for layout, cap, m in ((W.BINNED, 2, None), (W.PADDED, None, 4)):
+                r = o.route_prep(top, E, pad_multiple=m)
+                rows, R = brute_rows(top, E, layout, capacity=cap, pad_multiple=m)
+                dout = W.normal(rng, (T, 5), dtype)
+                y64 = torch.zeros((R, 5), dtype=torch.float64, requires_grad=True)
+                out = _torch_combine(y64, rows, torch.from_numpy(w.reshape(-1).astype(np.float64)), T, K)
+                (out * torch.from_numpy(W.to_f32(dout, dtype).astype(np.float64))).sum().backward()
+                dy = o.combine_backward_dy(dout, dtype, r, layout, cap, weights=w.reshape(-1))
+                assert _ulp_close(dy, y64.grad.numpy(), dtype), "combine backward vs autograd"
+                unused = np.ones(R, bool)
+                unused[rows[rows >= 0]] = False
+                assert np.all(W.to_f32(dy, dtype)[unused] == 0)
+                plain = o.combine_backward_dy(dout, dtype, r, layout, cap)
+                assert np.array_equal(plain.view(np.uint8), o.gather(dout, r, layout, cap).view(np.uint8))
+                sample = np.array([R - 1, 0, R // 2], np.int64)
+                assert np.array_equal(o.combine_backward_dy(dout, dtype, r, layout, cap, weights=w.reshape(-1),
+                                                            rows=sample).view(np.uint8), dy[sample].view(np.uint8))
+
+
 # ----------------------------------------------------------------------------
 # Routing-map compaction.
 # ----------------------------------------------------------------------------
@@ -512,4 +541,4 @@ def pin_validate(o):
 ALL_PINS = [pin_bf16_rounding, pin_f16_rounding, pin_widening, pin_route_prep_numpy, pin_route_prep_exhaustive,
             pin_route_prep_invariants, pin_golden, pin_gather_numpy, pin_gather_bits_and_identity,
             pin_scatter_closed_form, pin_scatter_random_y, pin_wgrad_autograd, pin_wgrad_closed_form,
-            pin_sampled_tokens, pin_compaction, pin_validate]
+            pin_sampled_tokens, pin_combine_backward, pin_compaction, pin_validate]

@@ -41,6 +41,8 @@ MUTANTS = [
     ("wgrad_drops_h0", "for (int64_t h = 0; h < H; ++h) {\n                double p =",
      "for (int64_t h = 1; h < H; ++h) {\n                double p =", 0),
     ("wgrad_slot_k_reversed", "int64_t i = pos_of[t * K + k];", "int64_t i = pos_of[t * K + (K - 1 - k)];", 0),
+    ("dy_weight_dropped", "double w = (double)weights[a];", "double w = 1.0;", 0),
+    ("dy_token_shift", "int64_t t = a / K;", "int64_t t = (a / K + 1) % T;", 0),
     ("bf16_ties_away", "double r = nearbyint(m);", "double r = floor(m + 0.5);", 0),
     ("f16_subnormal_scale", "uint16_t fr = (uint16_t)ldexp(r, 24);", "uint16_t fr = (uint16_t)ldexp(r, 23);", 0),
     ("f16_decode_exponent", "ex - 25); /* (1 + fr/1024)", "ex - 24); /* (1 + fr/1024)", 0),
