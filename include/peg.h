@@ -212,6 +212,33 @@ peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int32_t lay
                      void* stream);
 
 /*
+ * peg_combine_backward - backward of the combine fused with wgrad.
+ * The combine ([BIN] Workflow step 5, [PAD] Workflow step 6) is linear in the
+ * expert tensor; its gradient with respect to that tensor, given the upstream
+ * gradient dout of the combine output, sends dout back through the same row
+ * mapping (the [PAD] front matter lists this use of the padded storage).
+ * wgrad is [BIN]/[PAD] Workflow step 6 with grad = dout.
+ *
+ * One pass over dout computes both:
+ *   dy[row(a)] = w[a] * dout[a/K] for every kept assignment a (fp32 product,
+ *                one rounding to dtype; raw bit copy when weights == NULL);
+ *                every other row of [0, dy_rows) is zero (gap rows);
+ *   wgrad[a]   = <y[row(a)], dout[a/K]> as peg_wgrad.
+ *   y [R, H], dout [T, H], dy [dy_rows, H], all of dtype; weights [T*K] f32
+ *   or NULL; wgrad [T*K] f32, fully written. R = E*C (binned) or
+ *   padded_bins[E-1] (padded). Rows of dy at or past dy_rows are never
+ *   written (a route whose row is there gets no dy row; its wgrad is still
+ *   computed). The other arguments are as for peg_wgrad.
+ * Errors: NULL_ARG, BAD_SHAPE (also dy_rows < 0), BAD_DTYPE, ALIGNMENT,
+ * WORKSPACE, LAUNCH.
+ */
+peg_status peg_combine_backward(const void* y, const void* dout, const float* weights, int32_t dtype,
+                                int32_t layout, int64_t T, int64_t H, int32_t K, int32_t E, int32_t capacity,
+                                const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
+                                const int32_t* padded_bins, const int32_t* slot_row, void* dy, int64_t dy_rows,
+                                float* wgrad, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * peg_routing_map_compact - dense routing map -> fixed-width routes.
  * [MOK] RoutingMapToIndices and routing_map_to_mok_inputs.
  *

@@ -425,8 +425,8 @@ int pego_wgrad(const void* y, const void* grad, int32_t dtype, int64_t R, int64_
  * Its gradient with respect to y, given the upstream gradient dout [T, H],
  * is therefore: every kept sorted position i with assignment a = indices[i]
  * gets w[a] * dout[a / K] in its row (the weighted gather of dout through
- * the same mapping, "maps gradients through padded expert storage" in the
- * [PAD] description); every other row of the R-row tensor is zero. Without
+ * the same mapping; the [PAD] front matter lists this use of the padded
+ * storage); every other row of the R-row tensor is zero. Without
  * weights (factor 1) the rows are copied as raw bits. The product runs in
  * double and is rounded once to dtype. rows == NULL: dy holds all R rows;
  * otherwise dy[j] is row rows[j] (a sample).

@@ -8,7 +8,8 @@ without a GPU the calls raise.
 
 Functions (same names as the C entry points without the ``peg_`` prefix):
   route_prep, gather_binned, gather_padded, scatter_combine, wgrad,
-  routing_map_compact, routing_map_compact_backward, validate_routing.
+  combine_backward, routing_map_compact, routing_map_compact_backward,
+  validate_routing.
 """
 import ctypes
 import os
@@ -61,6 +62,8 @@ def _load():
                                  P, P, c_size_t, P], st),
         "peg_wgrad": ([P, P, c_int32, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, P, P, P, P, P, P, P,
                        c_size_t, P], st),
+        "peg_combine_backward": ([P, P, P, c_int32, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, P, P, P, P,
+                                  P, P, c_int64, P, P, c_size_t, P], st),
         "peg_routing_map_compact": ([P, c_int32, P, c_int64, c_int32, c_int32, P, P, P], st),
         "peg_routing_map_compact_backward": ([P, P, c_int64, c_int32, c_int32, P, P], st),
         "peg_validate_routing": ([P, P, P, P, c_int64, c_int32, c_int32, c_int64, P, P, c_size_t, P], st),
@@ -268,6 +271,36 @@ def wgrad(y, grad, r, out=None, ws=None, use_slot_row=True):
                                _stream(y.device))
     _check(st, "wgrad")
     return out
+
+
+def combine_backward(y, dout, r, weights=None, dy=None, dy_rows=None, wgrad_out=None, ws=None, use_slot_row=True):
+    """Backward of the combine fused with wgrad: returns (dy, wgrad) where
+    dy[row(a)] = w[a] * dout[t] in the expert layout (gap rows zero; a raw copy
+    when weights is None) and wgrad [T, K] f32 = <y[row(a)], dout[t]>."""
+    y = _dev(y, "y")
+    dout = _dev(dout, "dout", y.dtype)
+    H = y.shape[1]
+    if dout.shape != (r.T, H):
+        raise ValueError("dout must be [T, H]")
+    if weights is not None:
+        weights = _dev(weights, "weights", torch.float32)
+        if weights.numel() != r.T * r.K:
+            raise ValueError("weights must hold T*K values")
+    if dy is None:
+        rows = dy_rows if dy_rows is not None else (r.E * r.capacity if r.layout == BINNED else r.expert_rows())
+        dy = torch.empty((rows, H), dtype=y.dtype, device=y.device)
+    _dev(dy, "dy", y.dtype)
+    if wgrad_out is None:
+        wgrad_out = torch.empty((r.T, r.K), dtype=torch.float32, device=y.device)
+    _dev(wgrad_out, "wgrad_out", torch.float32)
+    ws, wsb = _ws(r.T, r.K, r.E, y.device, ws)
+    with torch.cuda.device(y.device):
+        st = _load().peg_combine_backward(_ptr(y), _ptr(dout), _ptr(weights), _dtype_code(y, "y"), r.layout, r.T, H,
+                                          r.K, r.E, int(r.capacity or 0), _ptr(r.indices), _ptr(r.bin_ids),
+                                          _ptr(r.bins), _ptr(r.padded_bins), _ptr(_slot(r, use_slot_row)), _ptr(dy),
+                                          dy.shape[0], _ptr(wgrad_out), _ptr(ws), wsb, _stream(y.device))
+    _check(st, "combine_backward")
+    return dy, wgrad_out
 
 
 def routing_map_compact(probs, routing_map, topk, probs_out=None, route_experts=None):

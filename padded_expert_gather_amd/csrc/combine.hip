@@ -18,6 +18,7 @@
 // finish with a wave64 butterfly and a sum over the token's waves in LDS.
 // Rows that are
 // unused capacity, padding or dropped are never read.
+#include "gaps.hpp"
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
@@ -132,16 +133,32 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
 // wgrad: each wave dots its slice of the token's columns for up to 8 routes
 // at a time; partial dots finish with a wave64 butterfly and a sum over the
 // token's WPT waves in LDS.
-template <int DT, int VEC, int U, int WPT>
+//
+// DY != 0 is the backward of the combine fused with wgrad: `grad` is then the
+// upstream gradient of the combine output, and while each of its vectors is
+// in registers it is also stored into the gradient of the expert tensor, dy,
+// at every kept row of the token - scaled by that route's weight (DY == 2)
+// or as raw bits (DY == 1). Blocks past token_blocks zero dy's gap rows.
+template <int DT, int VEC, int U, int WPT, int DY>
 __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
                                                        float* __restrict__ wgrad, int64_t nch, int64_t slice,
                                                        int64_t T, int32_t K, const int32_t* __restrict__ slot_row,
                                                        int64_t static_rows, const int32_t* __restrict__ padded_bins,
-                                                       int32_t E) {
+                                                       int32_t E, const float* __restrict__ weights,
+                                                       uint8_t* __restrict__ dy, int64_t dy_rows, int32_t layout,
+                                                       int32_t capacity, const int32_t* __restrict__ bins,
+                                                       int64_t token_blocks) {
     using L = Lanes<DT, VEC>;
     using V = typename L::V;
     constexpr int N = L::N;
     constexpr int NW = kBlock / kWave;
+    if constexpr (DY != 0) {
+        if ((int64_t)blockIdx.x >= token_blocks) {
+            zero_gap_rows<VEC>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins,
+                               (int64_t)blockIdx.x - token_blocks, (int64_t)gridDim.x - token_blocks);
+            return;
+        }
+    }
     __shared__ float red[NW][kRowsFast];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int TPB = TokenMap<WPT>::kTokensPerBlock;
@@ -157,11 +174,13 @@ __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict
 
     for (int k0 = 0; k0 < K; k0 += kRowsFast) {
         int r8[kRowsFast];
+        float w8[kRowsFast];
         bool any = false;
 #pragma unroll
         for (int k = 0; k < kRowsFast; ++k) {
             r8[k] = active ? route_row(my_rows, k0 + k, K, R) : -1;
             any |= r8[k] >= 0;
+            if constexpr (DY == 2) w8[k] = r8[k] >= 0 ? weights[(active ? t : 0) * K + k0 + k] : 0.0f;
         }
         float acc[kRowsFast];
 #pragma unroll
@@ -190,16 +209,31 @@ __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        if (c0 + u * kWave + lane >= c_end) continue;
+                        const int64_t c = c0 + u * kWave + lane;
+                        if (c >= c_end) continue;
                         float g[N];
                         L::unpack(gv[u], g);
 #pragma unroll
                         for (int kk = 0; kk < kKBatch; ++kk) {
-                            if (r8[kb + kk] < 0) continue;
+                            const int r = r8[kb + kk];
+                            if (r < 0) continue;
                             float f[N];
                             L::unpack(v[kk][u], f);
 #pragma unroll
                             for (int i = 0; i < N; ++i) acc[kb + kk] = fmaf(f[i], g[i], acc[kb + kk]);
+                            if constexpr (DY != 0) {
+                                if (r < dy_rows) {
+                                    uint8_t* drow = dy + (int64_t)r * row_bytes;
+                                    if constexpr (DY == 1) {
+                                        stream_store<VEC>(drow, c, gv[u]);
+                                    } else {
+                                        float o[N];
+#pragma unroll
+                                        for (int i = 0; i < N; ++i) o[i] = w8[kb + kk] * g[i];
+                                        stream_store<VEC>(drow, c, L::pack(o));
+                                    }
+                                }
+                            }
                         }
                     }
                 }
@@ -306,39 +340,59 @@ static peg_status combine_dispatch(int vec, hipStream_t s, const uint8_t* y, uin
     }
 }
 
-template <int DT, int VEC>
-static peg_status wgrad_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg,
-                            int64_t nch, int64_t q, int64_t T, int32_t K, const int32_t* slot_row, RowArgs ra,
-                            int32_t E) {
-    if (u == 1)
-        return launch(wgrad_kernel<DT, VEC, 1, PEG_WGRAD_WPT>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, T, K,
-                      slot_row, ra.static_rows, ra.padded_bins, E);
-    if (u == 2)
-        return launch(wgrad_kernel<DT, VEC, 2, PEG_WGRAD_WPT>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, T, K,
-                      slot_row, ra.static_rows, ra.padded_bins, E);
+// Arguments of the wgrad / fused-backward launch.
+struct WgradArgs {
+    const uint8_t* y;
+    const uint8_t* g;
+    float* wg;
+    int64_t nch, slice, T;
+    int32_t K;
+    const int32_t* slot_row;
+    RowArgs ra;
+    int32_t E;
+    const float* weights;
+    uint8_t* dy;
+    int64_t dy_rows;
+    int32_t layout, capacity;
+    const int32_t* bins;
+    int64_t token_blocks;
+};
+
+template <int DT, int VEC, int U, int DY>
+static peg_status wgrad_go(dim3 grid, hipStream_t s, const WgradArgs& a) {
+    return launch(wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT, DY>, grid, dim3(kBlock), 0, s, a.y, a.g, a.wg, a.nch,
+                  a.slice, a.T, a.K, a.slot_row, a.ra.static_rows, a.ra.padded_bins, a.E, a.weights, a.dy,
+                  a.dy_rows, a.layout, a.capacity, a.bins, a.token_blocks);
+}
+
+template <int DT, int VEC, int DY>
+static peg_status wgrad_u(int u, dim3 grid, hipStream_t s, const WgradArgs& a) {
+    if (u == 1) return wgrad_go<DT, VEC, 1, DY>(grid, s, a);
+    if (u == 2) return wgrad_go<DT, VEC, 2, DY>(grid, s, a);
 #if PEG_WGRAD_UMAX >= 4
-    return launch(wgrad_kernel<DT, VEC, 4, PEG_WGRAD_WPT>, grid, dim3(kBlock), 0, s, y, g, wg, nch, q, T, K,
-                  slot_row, ra.static_rows, ra.padded_bins, E);
+    return wgrad_go<DT, VEC, 4, DY>(grid, s, a);
 #else
     return PEG_ERR_LAUNCH;
 #endif
 }
 
-template <int DT>
-static peg_status wgrad_dispatch(int vec, hipStream_t s, const uint8_t* y, const uint8_t* g, float* wg, int64_t nch,
-                                 int64_t T, int32_t K, const int32_t* slot_row, RowArgs ra, int32_t E) {
-    const int64_t q = wave_slice(nch, PEG_WGRAD_WPT);
-    const int u = pass_vectors(q, PEG_WGRAD_UMAX);
-    const dim3 grid((unsigned)token_blocks(T, PEG_WGRAD_WPT));
+template <int DT, int DY>
+static peg_status wgrad_dispatch(int vec, int u, dim3 grid, hipStream_t s, const WgradArgs& a) {
     switch (vec) {
-        case 16: return wgrad_vec<DT, 16>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
-        case 8: return wgrad_vec<DT, 8>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
-        case 4: return wgrad_vec<DT, 4>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
+        case 16: return wgrad_u<DT, 16, DY>(u, grid, s, a);
+        case 8: return wgrad_u<DT, 8, DY>(u, grid, s, a);
+        case 4: return wgrad_u<DT, 4, DY>(u, grid, s, a);
         default:
-            if constexpr (Elem<DT>::bytes == 2)
-                return wgrad_vec<DT, 2>(u, grid, s, y, g, wg, nch, q, T, K, slot_row, ra, E);
+            if constexpr (Elem<DT>::bytes == 2) return wgrad_u<DT, 2, DY>(u, grid, s, a);
             return PEG_ERR_ALIGNMENT;
     }
+}
+
+template <int DY>
+static peg_status wgrad_by_dtype(int32_t dtype, int vec, int u, dim3 grid, hipStream_t s, const WgradArgs& a) {
+    if (dtype == PEG_F32) return wgrad_dispatch<PEG_F32, DY>(vec, u, grid, s, a);
+    if (dtype == PEG_BF16) return wgrad_dispatch<PEG_BF16, DY>(vec, u, grid, s, a);
+    return wgrad_dispatch<PEG_F16, DY>(vec, u, grid, s, a);
 }
 
 }  // namespace peg
@@ -383,9 +437,39 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const uint8_t* yb = (const uint8_t*)y;
-    const uint8_t* gb = (const uint8_t*)grad;
-    if (dtype == PEG_F32) return wgrad_dispatch<PEG_F32>(vec, s, yb, gb, wgrad, nch, T, K, slot_row, ra, E);
-    if (dtype == PEG_BF16) return wgrad_dispatch<PEG_BF16>(vec, s, yb, gb, wgrad, nch, T, K, slot_row, ra, E);
-    return wgrad_dispatch<PEG_F16>(vec, s, yb, gb, wgrad, nch, T, K, slot_row, ra, E);
+    const int64_t q = wave_slice(nch, PEG_WGRAD_WPT);
+    const int u = pass_vectors(q, PEG_WGRAD_UMAX);
+    const int64_t tb = token_blocks(T, PEG_WGRAD_WPT);
+    const WgradArgs a{(const uint8_t*)y, (const uint8_t*)grad, wgrad, nch, q, T, K, slot_row, ra, E, nullptr,
+                      nullptr, 0, layout, capacity, bins, tb};
+    return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
+}
+
+PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const float* weights, int32_t dtype,
+                                        int32_t layout, int64_t T, int64_t H, int32_t K, int32_t E, int32_t capacity,
+                                        const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
+                                        const int32_t* padded_bins, const int32_t* slot_row, void* dy,
+                                        int64_t dy_rows, float* wgrad, void* ws, size_t ws_bytes, void* stream) {
+    PEG_CHECK(check_common(dtype, layout, T, H, K, E, capacity, padded_bins));
+    if (dy_rows < 0 || dy_rows > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    if (!bins || (T > 0 && (!y || !dout || !wgrad)) || (dy_rows > 0 && !dy)) return PEG_ERR_NULL_ARG;
+    const int eb = elem_bytes(dtype);
+    if (!aligned(y, eb) || !aligned(dout, eb) || !aligned(dy, eb) || !aligned(wgrad, 4) ||
+        (weights && !aligned(weights, 4)))
+        return PEG_ERR_ALIGNMENT;
+    const int vec = pick_vec(H * eb, eb, y, dout, dy);
+    if (vec == 0) return PEG_ERR_ALIGNMENT;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    PEG_CHECK(ensure_slots(T, K, E, layout, capacity, indices, bin_ids, bins, padded_bins, &slot_row, ws, ws_bytes, s));
+    const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
+                     layout == PEG_PADDED ? padded_bins : nullptr};
+    const int64_t nch = H * eb / vec;
+    const int64_t q = wave_slice(nch, PEG_WGRAD_WPT);
+    const int u = pass_vectors(q, PEG_WGRAD_UMAX);
+    const int64_t tb = token_blocks(T, PEG_WGRAD_WPT);
+    const dim3 grid((unsigned)(tb + gap_blocks(dy_rows, nch)));
+    const WgradArgs a{(const uint8_t*)y, (const uint8_t*)dout, wgrad, nch, q, T, K, slot_row, ra, E, weights,
+                      (uint8_t*)dy, dy_rows, layout, capacity, bins, tb};
+    if (weights) return wgrad_by_dtype<2>(dtype, vec, u, grid, s, a);
+    return wgrad_by_dtype<1>(dtype, vec, u, grid, s, a);
 }

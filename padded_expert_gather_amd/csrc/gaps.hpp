@@ -1,0 +1,108 @@
+// gaps.hpp - zeroing of the gap rows of an expert tensor: the unused
+// capacity of the binned layout ("Build Triton-Ascend Binned MoE Routing",
+// Ascend Guardrails: zero-initialised output) and the padding of the padded
+// layout ("Build Triton-Ascend Padded MoE Routing", Ascend Guardrails: zero
+// gaps). Only gap rows are written, once; each expert's gap is one contiguous
+// byte range.
+#pragma once
+
+#include "peg_device.hpp"
+#include "peg_host.hpp"
+
+namespace peg {
+
+#ifndef PEG_GAP_UNITS
+#define PEG_GAP_UNITS 8192  // target vectors zeroed per gap block
+#endif
+#ifndef PEG_GAP_MAX
+#define PEG_GAP_MAX 2048  // most gap blocks per launch
+#endif
+constexpr int kZeroUnroll = 4;
+
+// Gap blocks for a tensor of up to max_gap_rows gap rows of nch vectors.
+inline int64_t gap_blocks(int64_t max_gap_rows, int64_t nch) {
+    const int64_t units = max_gap_rows * nch;
+    int64_t b = (units + PEG_GAP_UNITS - 1) / PEG_GAP_UNITS;
+    if (b < 1) b = 1;
+    if (b > PEG_GAP_MAX) b = PEG_GAP_MAX;
+    return b;
+}
+
+// Block zb of nz gap blocks zeroes its share of the gap rows of `out`
+// (out_rows rows of nch VEC-byte vectors). Binned: expert e's rows
+// [e*C + min(count, C), (e+1)*C); padded: [pstart(e) + count, padded_bins[e]).
+// Whole block must call it (contains barriers).
+template <int VEC>
+__device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t nch, int64_t out_rows,
+                                              int32_t layout, int32_t E, int32_t capacity,
+                                              const int32_t* __restrict__ bins,
+                                              const int32_t* __restrict__ padded_bins, int64_t zb, int64_t nz) {
+    using V = typename VecOf<VEC>::T;
+    // gap of expert e = rows [gstart[e], gstart[e] + glen[e]); gpre = exclusive
+    // prefix of glen. Rows at or past out_rows are never touched.
+    __shared__ int gpre[PEG_MAX_EXPERTS + 1];
+    __shared__ int gstart[PEG_MAX_EXPERTS];
+    __shared__ int scratch[kBlock / kWave];
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kBlock) {
+        const int e = e0 + threadIdx.x;
+        int len = 0, start = 0;
+        if (e < E) {
+            int count = bins[e] - (e ? bins[e - 1] : 0);
+            count = count < 0 ? 0 : count;
+            int64_t s, g;
+            if (layout == PEG_BINNED) {
+                const int kept = count < capacity ? count : capacity;
+                s = (int64_t)e * capacity + kept;
+                g = capacity - kept;
+            } else {
+                const int64_t ps = e ? padded_bins[e - 1] : 0;
+                s = ps + count;
+                g = (int64_t)padded_bins[e] - s;
+            }
+            if (g <= 0 || s < 0 || s >= out_rows) g = 0;   // no gap, or it starts past the buffer
+            else if (s + g > out_rows) g = out_rows - s;   // gap cut at the end of the buffer
+            len = (int)g;
+            start = (int)(g > 0 ? s : 0);
+        }
+        int total;
+        int pre = block_exclusive_scan<kBlock>(len, scratch, &total);
+        if (e < E) {
+            gpre[e] = carry + pre;
+            gstart[e] = start;
+        }
+        carry += total;
+    }
+    if (threadIdx.x == 0) gpre[E] = carry;
+    lds_barrier();
+
+    const int64_t units = (int64_t)carry * nch;
+    const int64_t lo = units * zb / nz;
+    const int64_t hi = units * (zb + 1) / nz;
+    if (lo >= hi) return;
+    // first expert whose gap holds unit lo: last e with gpre[e] * nch <= lo
+    int a = 0, b = E - 1;
+    while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if ((int64_t)gpre[mid] * nch <= lo) a = mid;
+        else b = mid - 1;
+    }
+    // walk this block's range one expert gap (a contiguous byte range) at a
+    // time, kZeroUnroll stores in flight per thread
+    const V z = zero_vec<VEC>();
+    int64_t u0 = lo;
+    for (int e = a; u0 < hi && e < E; ++e) {
+        const int64_t seg_end = (int64_t)gpre[e + 1] * nch < hi ? (int64_t)gpre[e + 1] * nch : hi;
+        const int64_t shift = (int64_t)gstart[e] * nch - (int64_t)gpre[e] * nch;  // unit -> output vector
+        for (int64_t u = u0 + threadIdx.x; u < seg_end; u += (int64_t)kBlock * kZeroUnroll) {
+#pragma unroll
+            for (int j = 0; j < kZeroUnroll; ++j) {
+                const int64_t uu = u + (int64_t)j * kBlock;
+                if (uu < seg_end) stream_store<VEC>(out, shift + uu, z);
+            }
+        }
+        u0 = seg_end > u0 ? seg_end : u0;
+    }
+}
+
+}  // namespace peg

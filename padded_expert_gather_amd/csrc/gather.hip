@@ -18,19 +18,11 @@
 //   * in the same launch, trailing "gap" blocks write zeros into the unused
 //     capacity / padding rows only (each gap of an expert is one contiguous
 //     byte range), so no row is written twice and no memset pass is needed.
+#include "gaps.hpp"
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
 namespace peg {
-
-// Launch-shape knobs (build-time; defaults measured on MI355X).
-#ifndef PEG_GAP_UNITS
-#define PEG_GAP_UNITS 8192  // target vectors zeroed per gap block
-#endif
-#ifndef PEG_GAP_MAX
-#define PEG_GAP_MAX 2048  // most gap blocks per launch
-#endif
-constexpr int kZeroUnroll = 4;
 
 // The columns of a token row are split into WPT contiguous slices, one per
 // wave; a wave moves its slice in passes of 64 lanes x U vectors.
@@ -104,73 +96,8 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     }
 
     // ---------------- zero the gap rows ----------------
-    // gap of expert e = rows [gstart[e], gstart[e] + glen[e]); gpre = exclusive
-    // prefix of glen. Rows at or past out_rows are never touched.
-    __shared__ int gpre[PEG_MAX_EXPERTS + 1];
-    __shared__ int gstart[PEG_MAX_EXPERTS];
-    __shared__ int scratch[kBlock / kWave];
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kBlock) {
-        const int e = e0 + threadIdx.x;
-        int len = 0, start = 0;
-        if (e < E) {
-            int count = bins[e] - (e ? bins[e - 1] : 0);
-            count = count < 0 ? 0 : count;
-            int64_t s, g;
-            if (layout == PEG_BINNED) {
-                const int kept = count < capacity ? count : capacity;
-                s = (int64_t)e * capacity + kept;
-                g = capacity - kept;
-            } else {
-                const int64_t ps = e ? padded_bins[e - 1] : 0;
-                s = ps + count;
-                g = (int64_t)padded_bins[e] - s;
-            }
-            if (g <= 0 || s < 0 || s >= out_rows) g = 0;   // no gap, or it starts past the buffer
-            else if (s + g > out_rows) g = out_rows - s;   // gap cut at the end of the buffer
-            len = (int)g;
-            start = (int)(g > 0 ? s : 0);
-        }
-        int total;
-        int pre = block_exclusive_scan<kBlock>(len, scratch, &total);
-        if (e < E) {
-            gpre[e] = carry + pre;
-            gstart[e] = start;
-        }
-        carry += total;
-    }
-    if (threadIdx.x == 0) gpre[E] = carry;
-    lds_barrier();
-
-    const int64_t units = (int64_t)carry * nch;
-    const int64_t nz = (int64_t)gridDim.x - token_blocks;
-    const int64_t zb = (int64_t)blockIdx.x - token_blocks;
-    const int64_t lo = units * zb / nz;
-    const int64_t hi = units * (zb + 1) / nz;
-    if (lo >= hi) return;
-    // first expert whose gap holds unit lo: last e with gpre[e] * nch <= lo
-    int a = 0, b = E - 1;
-    while (a < b) {
-        const int mid = (a + b + 1) >> 1;
-        if ((int64_t)gpre[mid] * nch <= lo) a = mid;
-        else b = mid - 1;
-    }
-    // walk this block's range one expert gap (a contiguous byte range) at a
-    // time, kZeroUnroll stores in flight per thread
-    const V z = zero_vec<VEC>();
-    int64_t u0 = lo;
-    for (int e = a; u0 < hi && e < E; ++e) {
-        const int64_t seg_end = (int64_t)gpre[e + 1] * nch < hi ? (int64_t)gpre[e + 1] * nch : hi;
-        const int64_t shift = (int64_t)gstart[e] * nch - (int64_t)gpre[e] * nch;  // unit -> output vector
-        for (int64_t u = u0 + threadIdx.x; u < seg_end; u += (int64_t)kBlock * kZeroUnroll) {
-#pragma unroll
-            for (int j = 0; j < kZeroUnroll; ++j) {
-                const int64_t uu = u + (int64_t)j * kBlock;
-                if (uu < seg_end) stream_store<VEC>(out, shift + uu, z);
-            }
-        }
-        u0 = seg_end > u0 ? seg_end : u0;
-    }
+    zero_gap_rows<VEC>(out, nch, out_rows, layout, E, capacity, bins, padded_bins,
+                       (int64_t)blockIdx.x - token_blocks, (int64_t)gridDim.x - token_blocks);
 }
 
 struct GatherArgs {
@@ -197,16 +124,6 @@ static peg_status gather_launch(int u, dim3 grid, hipStream_t s, const GatherArg
     if (u == 2) PEG_GATHER_U(2);
     PEG_GATHER_U(4);
 #undef PEG_GATHER_U
-}
-
-// Zero-fill blocks: enough that each writes a few hundred KB at most.
-static int64_t gap_blocks(int64_t max_gap_rows, int64_t nch, int vec) {
-    const int64_t units = max_gap_rows * nch;
-    int64_t b = (units + PEG_GAP_UNITS - 1) / PEG_GAP_UNITS;
-    (void)vec;
-    if (b < 1) b = 1;
-    if (b > PEG_GAP_MAX) b = PEG_GAP_MAX;
-    return b;
 }
 
 static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
@@ -236,7 +153,7 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
         slot_row = rebuilt;
     }
     const int64_t nch = row_bytes / vec;
-    const int64_t nz = gap_blocks(out_rows, nch, vec);
+    const int64_t nz = gap_blocks(out_rows, nch);
     const int wpt = gather_wpt(nch);
     const int64_t tb = token_blocks(T, wpt);
     const dim3 grid((unsigned)(tb + nz));

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
 

@@ -82,6 +82,11 @@ def test_small_configs_full(cid, seed):
     assert_close(to_host(peg.scatter_combine(yrg, rg, weights=w_g)), so2, S2, wl.dtype, "combine(y_rand)")
     wo2, WS2 = oracle.wgrad(yr, wl.grad, wl.dtype, ro, wl.layout, cap, with_scale=True)
     assert_close(to_host(peg.wgrad(yrg, gg, rg)), wo2, WS2, W.F32, "wgrad(y_rand)")
+    # backward of the combine fused with wgrad, upstream gradient = wl.grad
+    dyo = oracle.combine_backward_dy(wl.grad, wl.dtype, ro, wl.layout, cap, weights=w_o)
+    dyg, wgb = peg.combine_backward(yrg, gg, rg, weights=w_g, dy_rows=R)
+    assert_close(to_host(dyg), dyo, np.abs(W.to_f32(dyo, wl.dtype).astype(np.float64)), wl.dtype, "backward dy")
+    assert_close(to_host(wgb), wo2, WS2, W.F32, "backward wgrad")
     if cid == 1:
         assert sum(np.asarray(ro.tokens_per_expert) > wl.capacity) >= 1  # overflow present
 
@@ -165,4 +170,20 @@ def test_large_config(cid):
         wr = peg.wgrad(yrg, gg, rg)
         assert not bool(torch.isnan(wr).any()), "wgrad read an unused row"
         assert_close(to_host(wr[tg]), wo2, WS2, W.F32, "wgrad(y_rand) sample")
+    # backward of the combine fused with wgrad: every kept row of dy equals
+    # the fp32 product w * dout rounded once (computed here by torch on the
+    # device), every other row is zero; the fused wgrad equals the wgrad
+    # kernel bit for bit; a row sample against the oracle
+    dyg, wgb = peg.combine_backward(yg, gg, rg, weights=w_g, dy_rows=R)
+    kept_t = torch.from_numpy(kept.astype(np.int64)).to(DEV)
+    rk = torch.from_numpy(rows[kept].astype(np.int64)).to(DEV)
+    want_rows = (w_g[kept_t].unsqueeze(1) * gg[kept_t // wl.K].float()).to(gg.dtype)
+    assert torch.equal(dyg[rk].view(torch.int16), want_rows.view(torch.int16)), "backward dy kept rows"
+    gapm = torch.ones(R, dtype=torch.bool, device=DEV)
+    gapm[rk] = False
+    assert int(dyg[gapm].view(torch.int16).count_nonzero().item()) == 0, "backward dy gap rows"
+    assert torch.equal(wgb, wgg), "fused wgrad == wgrad kernel"
+    dyo_s = oracle.combine_backward_dy(wl.grad, wl.dtype, ro, wl.layout, cap, weights=w_o, rows=sample)
+    assert_close(to_host(dyg[torch.from_numpy(sample).to(DEV)]), dyo_s,
+                 np.abs(W.to_f32(dyo_s, wl.dtype).astype(np.float64)), wl.dtype, "backward dy sample")
     print(f"[config {cid}] done", flush=True)

@@ -147,8 +147,24 @@ def test_edge_case(c):
     assert_close(to_host(peg.wgrad(yrg, gg, rg, use_slot_row=False)), wo, WS, W.F32, "wgrad rebuilt map")
     wo2, WS2 = oracle.wgrad(yo, grad, dtype, ro, layout, cap, with_scale=True)
     assert_close(to_host(peg.wgrad(yg, gg, rg)), wo2, WS2, W.F32, "wgrad(gather(x))")
+    # --- backward of the combine fused with wgrad (dout = grad)
+    check_combine_backward(yrg, yr, grad, gg, w, wg, ro, rg, layout, cap, dtype, R)
     # --- the validator accepts what route_prep built
     assert int(peg.validate_routing(rg, n_indices=ro.n).item()) == 0
+
+
+def check_combine_backward(yrg, yr, grad, gg, w, wg, ro, rg, layout, cap, dtype, R):
+    """dy = w * dout at kept rows, zero elsewhere (tolerance: one rounding of
+    a product); dy without weights = gather(dout) bit for bit; the fused
+    wgrad equals the oracle's and, bit for bit, the stand-alone kernel's."""
+    dyo = oracle.combine_backward_dy(grad, dtype, ro, layout, cap, weights=w.reshape(-1))
+    dyg, wgb = peg.combine_backward(yrg, gg, rg, weights=wg, dy_rows=R)
+    assert_close(to_host(dyg), dyo, np.abs(W.to_f32(dyo, dtype).astype(np.float64)), dtype, "combine backward dy")
+    wo, WS = oracle.wgrad(yr, grad, dtype, ro, layout, cap, with_scale=True)
+    assert_close(to_host(wgb), wo, WS, W.F32, "combine backward wgrad")
+    bits_equal(to_host(wgb), to_host(peg.wgrad(yrg, gg, rg)), "fused wgrad == wgrad kernel")
+    dyp, _ = peg.combine_backward(yrg, gg, rg, dy_rows=R, use_slot_row=False)
+    bits_equal(to_host(dyp), oracle.gather(grad, ro, layout, cap), "unweighted combine backward == gather")
 
 
 def test_gather_preserves_bit_patterns():
