@@ -12,13 +12,16 @@ Printed: one JSON line. ``value`` is the effective HBM bandwidth of the step,
 (algorithmic bytes of gather + combine + wgrad) / (wall time of the step,
 route_prep and compaction included); ``roofline`` is the dominant kernel's
 algorithmic bytes / its average duration (HIP events on its stream);
-``cpu_baseline`` is the CPU oracle on the same workload.
+``cpu_baseline`` is the CPU oracle on the same workload. ``backward`` times,
+outside the step, the backward of the combine fused with wgrad on the same
+buffers (dy in the expert layout + the routing-weight gradient).
 
 Algorithmic bytes per launch (s = element bytes, U = tokens with a kept
 route, N = kept assignments, R = expert-tensor rows):
   gather  = U*H*s + R*H*s + 4*T*K + 8*E
   combine = N*H*s + T*H*s + 8*T*K
   wgrad   = N*H*s + U*H*s + 8*T*K
+  combine backward = N*H*s (y) + U*H*s (dout) + R*H*s (dy) + 12*T*K
 """
 import argparse
 import ctypes
@@ -41,7 +44,7 @@ def log(msg):
 
 
 KERNEL_SOURCES = {"gather": "gather.hip", "combine": "combine.hip", "wgrad": "combine.hip",
-                  "route_prep": "route_prep.hip", "compact": "compact.hip"}
+                  "backward": "combine.hip", "route_prep": "route_prep.hip", "compact": "compact.hip"}
 
 
 def source_hash(kernel=None):
@@ -72,6 +75,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device-to-device copies (reference for the HBM byte counters) and exit")
     return ap.parse_args()
@@ -152,6 +156,8 @@ class Step:
         self.y = torch.empty((self.R, H), dtype=tdt, device=dev)
         self.out = torch.empty((T, H), dtype=tdt, device=dev)
         self.wg = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.dy = None if host.get("no_backward") else torch.empty((self.R, H), dtype=tdt, device=dev)
+        self.wg_b = torch.empty((T, K), dtype=torch.float32, device=dev)
         P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
         st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         self.stream = st
@@ -184,6 +190,22 @@ class Step:
                                 P(self.bin_ids), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.wg),
                                 P(self.ws), wsb, st))
         self.order = list(self.calls)
+        # not part of the step: the backward of the combine, dout = grad
+        if self.dy is not None:
+            self.backward = (lib.peg_combine_backward,
+                             (P(self.y), P(self.grad), P(self.w), wl.dtype, wl.layout, T, H, K, E, cap,
+                              P(self.indices), P(self.bin_ids), P(self.bins), P(self.padded_bins), P(self.slot_row),
+                              P(self.dy), self.R, P(self.wg_b), P(self.ws), wsb, st))
+
+    def run_backward(self, ev=None, hip=None):
+        fn, args = self.backward
+        if ev is not None:
+            hip.record(ev[0], self.stream)
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"combine_backward failed with status {rc}")
+        if ev is not None:
+            hip.record(ev[1], self.stream)
 
     def run(self, events=None, hip=None):
         for name in self.order:
@@ -233,6 +255,11 @@ def algorithmic_bytes(wl, sz, s):
         "combine": sz["N"] * H * s + T * H * s + 8 * T * K,
         "wgrad": sz["N"] * H * s + sz["U"] * H * s + 8 * T * K,
     }
+
+
+def backward_bytes(wl, sz, s):
+    T, H, K = wl.T, wl.H, wl.K
+    return sz["N"] * H * s + sz["U"] * H * s + sz["R"] * H * s + 12 * T * K
 
 
 def cpu_baseline(wl, W, seconds, bytes_step):
@@ -303,7 +330,8 @@ def main():
     s = 4 if wl.dtype == W.F32 else 2
     ab = algorithmic_bytes(wl, sz, s)
     bytes_step = sum(ab.values())
-    per_set = (wl.T * wl.H * s) * 3 + sz["R"] * wl.H * s
+    host["no_backward"] = args.no_backward
+    per_set = (wl.T * wl.H * s) * 3 + sz["R"] * wl.H * s * (1 if args.no_backward else 2)
     sets = args.sets or max(2, min(16, math.ceil(2 * 2 ** 30 / per_set)))
     log(f"R={sz['R']} N={sz['N']} U={sz['U']} step bytes={bytes_step / 1e6:.1f} MB, {sets} input copies")
     steps_obj = [Step(peg, torch, wl, dev, host) for _ in range(sets)]
@@ -353,6 +381,25 @@ def main():
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic_for(dominant, wl.name),
                     "bytes_per_launch": ab[dominant], "avg_us": kernels[dominant]["avg_us"]}
+    # Timed region 3 (outside the step): the fused combine backward alone, one
+    # launch per input copy in turn, a HIP event pair around each launch.
+    backward = None
+    if not args.no_backward:
+        hip = HipEvents()
+        bb = backward_bytes(wl, sz, s)
+        for i in range(max(2, args.warmup)):
+            steps_obj[i % sets].run_backward()
+        torch.cuda.synchronize()
+        bevs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            steps_obj[i % sets].run_backward(bevs[i], hip)
+        torch.cuda.synchronize()
+        ms = [hip.elapsed_ms(a, b) for a, b in bevs]
+        avg = sum(ms) / len(ms)
+        backward = {"kernel": "combine_backward", "avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
+                    "bytes": bb, "GBps": round(bb / (avg / 1e3) / 1e9, 1),
+                    "frac_peak": round(bb / (avg / 1e3) / 1e9 / PEAK_GBS, 4),
+                    "traffic": traffic_for("backward", wl.name)}
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -375,6 +422,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "backward": backward,
         "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},
     }
     print(json.dumps(line), flush=True)

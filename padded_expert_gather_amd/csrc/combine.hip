@@ -140,14 +140,13 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
 // at every kept row of the token - scaled by that route's weight (DY == 2)
 // or as raw bits (DY == 1). Blocks past token_blocks zero dy's gap rows.
 template <int DT, int VEC, int U, int WPT, int DY>
-__global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
-                                                       float* __restrict__ wgrad, int64_t nch, int64_t slice,
-                                                       int64_t T, int32_t K, const int32_t* __restrict__ slot_row,
-                                                       int64_t static_rows, const int32_t* __restrict__ padded_bins,
-                                                       int32_t E, const float* __restrict__ weights,
-                                                       uint8_t* __restrict__ dy, int64_t dy_rows, int32_t layout,
-                                                       int32_t capacity, const int32_t* __restrict__ bins,
-                                                       int64_t token_blocks) {
+__device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
+                                           float* __restrict__ wgrad, int64_t nch, int64_t slice, int64_t T,
+                                           int32_t K, const int32_t* __restrict__ slot_row, int64_t static_rows,
+                                           const int32_t* __restrict__ padded_bins, int32_t E,
+                                           const float* __restrict__ weights, uint8_t* __restrict__ dy,
+                                           int64_t dy_rows, int32_t layout, int32_t capacity,
+                                           const int32_t* __restrict__ bins, int64_t token_blocks) {
     using L = Lanes<DT, VEC>;
     using V = typename L::V;
     constexpr int N = L::N;
@@ -263,6 +262,29 @@ __global__ __launch_bounds__(kBlock) void wgrad_kernel(const uint8_t* __restrict
     }
 }
 
+// Same parameter list for both kernels, so one launcher serves them.
+#define PEG_WGRAD_PARAMS                                                                                      \
+    const uint8_t *__restrict__ y, const uint8_t *__restrict__ grad, float *__restrict__ wgrad, int64_t nch,  \
+        int64_t slice, int64_t T, int32_t K, const int32_t *__restrict__ slot_row, int64_t static_rows,       \
+        const int32_t *__restrict__ padded_bins, int32_t E, const float *__restrict__ weights,                \
+        uint8_t *__restrict__ dy, int64_t dy_rows, int32_t layout, int32_t capacity,                          \
+        const int32_t *__restrict__ bins, int64_t token_blocks
+#define PEG_WGRAD_ARGS \
+    y, grad, wgrad, nch, slice, T, K, slot_row, static_rows, padded_bins, E, weights, dy, dy_rows, layout, capacity, bins, token_blocks
+
+template <int DT, int VEC, int U, int WPT>
+__global__ __launch_bounds__(kBlock) void wgrad_kernel(PEG_WGRAD_PARAMS) {
+    wgrad_body<DT, VEC, U, WPT, 0>(PEG_WGRAD_ARGS);
+}
+
+// DY: 1 = dy rows are dout rows as bits (no weights), 2 = weighted.
+template <int DT, int VEC, int U, int WPT, int DY>
+__global__ __launch_bounds__(kBlock) void combine_backward_kernel(PEG_WGRAD_PARAMS) {
+    wgrad_body<DT, VEC, U, WPT, DY>(PEG_WGRAD_ARGS);
+}
+#undef PEG_WGRAD_PARAMS
+#undef PEG_WGRAD_ARGS
+
 struct RowArgs {
     int64_t static_rows;
     const int32_t* padded_bins;
@@ -360,9 +382,16 @@ struct WgradArgs {
 
 template <int DT, int VEC, int U, int DY>
 static peg_status wgrad_go(dim3 grid, hipStream_t s, const WgradArgs& a) {
-    return launch(wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT, DY>, grid, dim3(kBlock), 0, s, a.y, a.g, a.wg, a.nch,
-                  a.slice, a.T, a.K, a.slot_row, a.ra.static_rows, a.ra.padded_bins, a.E, a.weights, a.dy,
-                  a.dy_rows, a.layout, a.capacity, a.bins, a.token_blocks);
+#define PEG_WGRAD_LAUNCH(KERNEL)                                                                                 \
+    return launch(KERNEL, grid, dim3(kBlock), 0, s, a.y, a.g, a.wg, a.nch, a.slice, a.T, a.K, a.slot_row,        \
+                  a.ra.static_rows, a.ra.padded_bins, a.E, a.weights, a.dy, a.dy_rows, a.layout, a.capacity, a.bins, \
+                  a.token_blocks)
+    if constexpr (DY == 0) {
+        PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT>));
+    } else {
+        PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_WGRAD_WPT, DY>));
+    }
+#undef PEG_WGRAD_LAUNCH
 }
 
 template <int DT, int VEC, int DY>
