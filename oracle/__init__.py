@@ -59,6 +59,8 @@ def load_library(path):
     lib.pego_routing_map_compact.restype = c_int32
     lib.pego_routing_map_compact_backward.argtypes = [f32p, i32p, c_int64, c_int32, c_int32, f32p]
     lib.pego_routing_map_compact_backward.restype = c_int32
+    lib.pego_router_topk.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, i32p, f32p]
+    lib.pego_router_topk.restype = c_int32
     lib.pego_validate_routing.argtypes = [i32p, i32p, i32p, i32p, c_int64, c_int32, c_int32, c_int64]
     lib.pego_validate_routing.restype = c_uint32
     return lib
@@ -263,6 +265,25 @@ def routing_map_compact_backward(grad_probs_out, route_experts, E):
     if rc != 0:
         raise ValueError("oracle routing_map_compact_backward refused its arguments")
     return out
+
+
+SOFTMAX, SIGMOID = 0, 1
+
+
+def router_topk(logits, dtype, K, gating=SOFTMAX, normalize=True):
+    """[FMD] router top-k gating over scores [T, E] (f32, or bf16/f16 bits):
+    returns (top_experts int32 [T, K], highest score first, lower id first on
+    ties; weights f32 [T, K], softmax or sigmoid probabilities, renormalised
+    over the K choices when ``normalize``)."""
+    lg = np.ascontiguousarray(logits, dtype=_np_dtype(dtype))
+    T, E = lg.shape
+    top = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float32)
+    rc = _load().pego_router_topk(_vp(lg), dtype, T, E, K, gating, 1 if normalize else 0, _p(top, c_int32),
+                                  _p(w, c_float))
+    if rc != 0:
+        raise ValueError("oracle router_topk refused its arguments")
+    return top, w
 
 
 def validate_routing(indices, bin_ids, bins, padded_bins, T, K, E, n_indices):

@@ -12,6 +12,7 @@
  *   [BIN] "Build Triton-Ascend Binned MoE Routing"
  *   [PAD] "Build Triton-Ascend Padded MoE Routing"
  *   [MOK] "core.transformer.moe.megakernel.mok.route_adapter"
+ *   [FMD] "Fused MoE Dispatch (Triton, universal)"
  *
  * Parity status per function is stated in the function comments; each is
  * pinned by the CPU tests against brute force, library routines, closed
@@ -522,6 +523,84 @@ int pego_routing_map_compact_backward(const float* grad_probs_out, const int32_t
             if (e >= 0 && e < E) grad_probs[t * E + e] = grad_probs_out[t * topk + j];
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router top-k gating.                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Ranking of two router scores: NaN ranks below every number; numbers by
+ * value (so -0 and +0 tie). */
+static int score_above(double a, double b) {
+    if (isnan(a)) return 0;
+    if (isnan(b)) return 1;
+    return a > b;
+}
+
+/*
+ * [FMD] pipeline figure (router scores -> top-k gating -> permute) and Usage
+ * (gating "softmax" or "sigmoid"). The pages name the two gating functions
+ * and nothing more; the readings taken:
+ *   - the K experts of a token are its K highest scores, listed from the
+ *     highest down, the lower expert id first among equal scores; the
+ *     ranking uses the scores themselves (softmax and sigmoid are
+ *     increasing, so this is the ranking of the probabilities without the
+ *     ties that rounding them would add);
+ *   - softmax: p_e = exp(l_e - m) / sum_j exp(l_j - m) over all E experts,
+ *     m = the highest score; sigmoid: p_e = 1 / (1 + exp(-l_e));
+ *   - normalize != 0: the K weights are p / (sum of the K selected p), the
+ *     renormalisation the workloads' router uses; else the K weights are p.
+ * Everything is evaluated in double in that order and rounded once to
+ * float32; NaN or infinite scores give whatever those formulas give.
+ * gating: 0 = softmax, 1 = sigmoid.
+ */
+int pego_router_topk(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,
+                     int32_t gating, int32_t normalize, int32_t* top_experts, float* weights) {
+    if (!dtype_ok(dtype) || T < 0 || E < 1 || K < 1 || K > E || (gating != 0 && gating != 1) ||
+        (T > 0 && (!logits || !top_experts || !weights)))
+        return -1;
+    double* l = (double*)malloc(sizeof(double) * (size_t)E);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    double* p = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!l || !taken || !p) {
+        free(l);
+        free(taken);
+        free(p);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            l[e] = pego_load(logits, dtype, t * E + e);
+            taken[e] = 0;
+        }
+        /* selection: K rounds, each takes the best remaining expert; the scan
+         * runs over increasing ids and replaces only on a strictly higher
+         * rank, so the lower id wins a tie */
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || score_above(l[e], l[best])) best = e;
+            }
+            taken[best] = 1;
+            top_experts[t * K + k] = best;
+        }
+        if (gating == 0) {
+            double m = l[top_experts[t * K]];
+            double denom = 0.0;
+            for (int32_t e = 0; e < E; ++e) denom += exp(l[e] - m);
+            for (int32_t k = 0; k < K; ++k) p[k] = exp(l[top_experts[t * K + k]] - m) / denom;
+        } else {
+            for (int32_t k = 0; k < K; ++k) p[k] = 1.0 / (1.0 + exp(-l[top_experts[t * K + k]]));
+        }
+        double sel = 0.0;
+        for (int32_t k = 0; k < K; ++k) sel += p[k];
+        for (int32_t k = 0; k < K; ++k) weights[t * K + k] = (float)(normalize ? p[k] / sel : p[k]);
+    }
+    free(l);
+    free(taken);
+    free(p);
     return 0;
 }
 

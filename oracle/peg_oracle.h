@@ -12,6 +12,8 @@
  *   [PAD] "Build Triton-Ascend Padded MoE Routing": same sections.
  *   [MOK] "core.transformer.moe.megakernel.mok.route_adapter":
  *         RoutingMapToIndices, routing_map_to_mok_inputs.
+ *   [FMD] "Fused MoE Dispatch (Triton, universal)": pipeline figure, Usage
+ *         (router top-k gating, softmax or sigmoid).
  * Floating point is evaluated in double (fp64) and rounded once to the
  * output type with round-to-nearest-even.
  *
@@ -72,6 +74,10 @@ int pego_routing_map_compact(const void* probs, int32_t probs_dtype, const uint8
 
 int pego_routing_map_compact_backward(const float* grad_probs_out, const int32_t* route_experts,
                                       int64_t T, int32_t E, int32_t topk, float* grad_probs);
+
+/* Router top-k gating: gating 0 = softmax, 1 = sigmoid; K <= E. */
+int pego_router_topk(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,
+                     int32_t gating, int32_t normalize, int32_t* top_experts, float* weights);
 
 uint32_t pego_validate_routing(const int32_t* indices, const int32_t* bin_ids,
                                const int32_t* bins, const int32_t* padded_bins, int64_t T,

@@ -513,6 +513,105 @@ def pin_compaction(o):
 
 
 # ----------------------------------------------------------------------------
+# Router top-k gating.
+# ----------------------------------------------------------------------------
+
+def _brute_rank(row):
+    """Experts of one score row in rank order, by a full sort: numbers by
+    decreasing value (-0 and +0 equal), then NaN, lower id first on ties."""
+    return sorted(range(len(row)), key=lambda e: (1, 0.0, e) if math.isnan(row[e]) else (0, -float(row[e]), e))
+
+
+def _f32_ulps(a, b):
+    """Distance in float32 units in the last place (finite, same sign)."""
+    ia = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+def pin_router_selection(o):
+    """Top-k selection vs a full sort on rows full of ties, signed zeros,
+    infinities and NaN, in all three score formats."""
+    rng = np.random.default_rng(91)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1.0, -1.0, 2.0], np.float32)
+    for E, K in [(1, 1), (5, 2), (8, 8), (16, 3), (64, 8), (70, 5), (257, 9)]:
+        T = 24
+        base = rng.integers(-3, 4, size=(T, E)).astype(np.float32)  # many exact ties
+        pick = rng.random((T, E)) < 0.15
+        base[pick] = specials[rng.integers(0, len(specials), size=int(pick.sum()))]
+        base[0] = np.nan                       # a row of NaN only
+        base[1] = -np.inf                      # a row of -inf only
+        for dtype in (W.F32, W.BF16, W.F16):
+            lg = W.cast_from_f32(base, dtype)  # exact: small integers and specials
+            top, _ = o.router_topk(lg, dtype, K)
+            for t in range(T):
+                assert list(top[t]) == _brute_rank(base[t])[:K], (E, K, dtype, t)
+            top_s, _ = o.router_topk(lg, dtype, K, gating=o.SIGMOID)
+            assert np.array_equal(top_s, top)  # the ranking does not depend on the gating
+
+
+def pin_router_weights_library(o):
+    """Weights vs scipy.special.softmax (and the logistic function from
+    scipy.special.expit) in float64, rounded to float32: equal within one
+    float32 ulp (both are double evaluations rounded once); large offsets
+    included, where exp without the maximum shift overflows."""
+    from scipy.special import expit, softmax
+    rng = np.random.default_rng(92)
+    for E, K, off in [(8, 2, 0.0), (64, 8, 0.0), (256, 8, 0.0), (33, 33, 0.0), (8, 2, 800.0), (16, 4, -900.0)]:
+        T = 16
+        lg = (rng.standard_normal((T, E)) * 3 + off).astype(np.float32)
+        for gating in (o.SOFTMAX, o.SIGMOID):
+            for norm in (True, False):
+                top, w = o.router_topk(lg, W.F32, K, gating=gating, normalize=norm)
+                for t in range(T):
+                    sel = np.array(_brute_rank(lg[t])[:K])
+                    assert np.array_equal(top[t], sel)
+                    x = lg[t].astype(np.float64)
+                    p = softmax(x)[sel] if gating == o.SOFTMAX else expit(x[sel])
+                    if norm:
+                        with np.errstate(invalid="ignore"):
+                            p = p / p.sum()
+                    want = p.astype(np.float32)
+                    nan = np.isnan(want)  # 0/0: every selected sigmoid underflowed
+                    assert np.array_equal(np.isnan(w[t]), nan), (E, K, off, gating, norm, t)
+                    ok = _f32_ulps(w[t][~nan], want[~nan]) <= 1
+                    assert ok.all(), (E, K, off, gating, norm, t, w[t], want)
+
+
+def pin_router_matches_workload_router(o):
+    """The 512-token workload's routing (numpy float32 softmax, stable argsort
+    of the probabilities, renormalised) is the oracle's softmax gating with
+    renormalisation: same experts (its probabilities have no ties), weights
+    within float32 evaluation error."""
+    wl = W.config(1, 0, with_rows=False)
+    top, w = o.router_topk(wl.logits, W.F32, wl.K)
+    assert np.array_equal(top, wl.top_experts)
+    assert np.all(np.abs(w.astype(np.float64) - wl.weights) <= 1e-6 * np.abs(wl.weights))
+
+
+def pin_router_closed_forms(o):
+    """Hand-worked values: scores (ln 6, ln 3, 0) give softmax (0.6, 0.3, 0.1)
+    and top-2 renormalised (2/3, 1/3); scores (ln 3, 0, -ln 3) give sigmoid
+    (0.75, 0.5, 0.25), renormalised (0.5, 1/3, 1/6); bf16 scores (0, 0)
+    tie -> experts (0, 1), weights (0.5, 0.5)."""
+    def near(got, want):
+        return bool(np.all(np.abs(np.asarray(got, np.float64) - np.asarray(want)) <= 2e-7 * np.abs(want)))
+
+    lg = np.array([[0.0, math.log(3.0), math.log(6.0)]], np.float32)
+    top, w = o.router_topk(lg, W.F32, 3, normalize=False)
+    assert list(top[0]) == [2, 1, 0] and near(w[0], [0.6, 0.3, 0.1])
+    top, w = o.router_topk(lg, W.F32, 2)
+    assert list(top[0]) == [2, 1] and near(w[0], [2 / 3, 1 / 3])
+    lg = np.array([[-math.log(3.0), 0.0, math.log(3.0)]], np.float32)
+    top, w = o.router_topk(lg, W.F32, 3, gating=o.SIGMOID, normalize=False)
+    assert list(top[0]) == [2, 1, 0] and near(w[0], [0.75, 0.5, 0.25])
+    top, w = o.router_topk(lg, W.F32, 3, gating=o.SIGMOID)
+    assert near(w[0], [0.5, 1 / 3, 1 / 6])
+    top, w = o.router_topk(np.zeros((1, 2), np.uint16), W.BF16, 2)
+    assert list(top[0]) == [0, 1] and list(w[0]) == [0.5, 0.5]
+
+
+# ----------------------------------------------------------------------------
 # Validation.
 # ----------------------------------------------------------------------------
 
@@ -541,4 +640,5 @@ def pin_validate(o):
 ALL_PINS = [pin_bf16_rounding, pin_f16_rounding, pin_widening, pin_route_prep_numpy, pin_route_prep_exhaustive,
             pin_route_prep_invariants, pin_golden, pin_gather_numpy, pin_gather_bits_and_identity,
             pin_scatter_closed_form, pin_scatter_random_y, pin_wgrad_autograd, pin_wgrad_closed_form,
-            pin_sampled_tokens, pin_combine_backward, pin_compaction, pin_validate]
+            pin_sampled_tokens, pin_combine_backward, pin_compaction, pin_router_selection,
+            pin_router_weights_library, pin_router_matches_workload_router, pin_router_closed_forms, pin_validate]

@@ -52,6 +52,15 @@ MUTANTS = [
      "pego_load(probs, probs_dtype, (int64_t)e * T + t)", 0),
     ("compact_backward_slot", "grad_probs[t * E + e] = grad_probs_out[t * topk + j];",
      "grad_probs[t * E + e] = grad_probs_out[t * topk + (topk - 1 - j)];", 0),
+    ("router_ties_to_higher_id", "if (best < 0 || score_above(l[e], l[best])) best = e;",
+     "if (best < 0 || !score_above(l[best], l[e])) best = e;", 0),
+    ("router_nan_ranks_high", "if (isnan(a)) return 0;", "if (isnan(a)) return 1;", 0),
+    ("router_no_max_shift", "denom += exp(l[e] - m);", "denom += exp(l[e]);", 0),
+    ("router_denominator_skips_last", "for (int32_t e = 0; e < E; ++e) denom", "for (int32_t e = 0; e + 1 < E; ++e) denom", 0),
+    ("router_sigmoid_sign", "1.0 / (1.0 + exp(-l[", "1.0 / (1.0 + exp(l[", 0),
+    ("router_normalize_ignored", "(float)(normalize ? p[k] / sel : p[k])", "(float)p[k]", 0),
+    ("router_selected_sum_first_only", "for (int32_t k = 0; k < K; ++k) sel += p[k];",
+     "for (int32_t k = 0; k < 1; ++k) sel += p[k];", 0),
     ("validate_no_duplicates", "if (seen[a]) flags |= FLAG_INDICES;", "(void)seen[a];", 0),
     ("validate_expected_off", "if (bins[e] <= i) ++expect;", "if (bins[e] < i) ++expect;", 0),
 ]

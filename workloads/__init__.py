@@ -100,6 +100,7 @@ class Workload:
     weights: np.ndarray = None       # [T, K] float32
     x: np.ndarray = None             # [T, H] dtype storage
     grad: np.ndarray = None          # [T, H] dtype storage
+    logits: np.ndarray = None        # [T, E] float32 router scores (bias included) the routing came from
     probs: np.ndarray = None         # [T, E] float32 (compaction configs)
     routing_map: np.ndarray = None   # [T, E] uint8 (compaction configs)
     topk: int = 0                    # compaction width
@@ -120,16 +121,18 @@ def config(cid, seed=0, with_rows=True):
     if cid == 1:
         # Binned, fp32, T512 H250 E8 K2, capacity = ceil(T*K/E) = 128.
         T, H, E, K = 512, 250, 8, 2
-        top, w = softmax_topk(rng.standard_normal((T, E), dtype=np.float32), K)
+        logits = rng.standard_normal((T, E), dtype=np.float32)
+        top, w = softmax_topk(logits, K)
         wl = Workload("binned-f32-T512-H250-E8-K2-C128", T, H, E, K, F32, BINNED,
-                      capacity=math.ceil(T * K / E), top_experts=top, weights=w, seed=seed)
+                      capacity=math.ceil(T * K / E), top_experts=top, weights=w, logits=logits, seed=seed)
         return _finish(rng, wl, with_rows)
     if cid == 2:
         # Padded, bf16, Mixtral-8x7B-shaped: T4096 H4096 E8 K2, multiple 128.
         T, H, E, K = 4096, 4096, 8, 2
-        top, w = softmax_topk(rng.standard_normal((T, E), dtype=np.float32), K)
+        logits = rng.standard_normal((T, E), dtype=np.float32)
+        top, w = softmax_topk(logits, K)
         wl = Workload("padded-bf16-T4096-H4096-E8-K2-m128", T, H, E, K, BF16, PADDED,
-                      pad_multiple=128, top_experts=top, weights=w, seed=seed)
+                      pad_multiple=128, top_experts=top, weights=w, logits=logits, seed=seed)
         return _finish(rng, wl, with_rows)
     if cid == 3:
         # Binned, bf16, Mixtral-8x22B-shaped: T16384 H6144 E8 K2, capacity factor
@@ -146,7 +149,7 @@ def config(cid, seed=0, with_rows=True):
         logits = rng.standard_normal((T, E), dtype=np.float32) + bias
         top, w = softmax_topk(logits, K)
         wl = Workload("binned-bf16-T16384-H6144-E8-K2-C5120", T, H, E, K, BF16, BINNED,
-                      capacity=math.ceil(1.25 * T * K / E), top_experts=top, weights=w, seed=seed,
+                      capacity=math.ceil(1.25 * T * K / E), top_experts=top, weights=w, logits=logits, seed=seed,
                       notes={"zipf_perm": perm.tolist()})
         return _finish(rng, wl, with_rows)
     if cid == 4:
@@ -173,7 +176,7 @@ def config(cid, seed=0, with_rows=True):
         logits = rng.standard_normal((T, E), dtype=np.float32) + bias
         top, w = softmax_topk(logits, K)
         wl = Workload("binned-bf16-T32768-H3584-E64-K8-C4096", T, H, E, K, BF16, BINNED,
-                      capacity=math.ceil(1.0 * T * K / E), top_experts=top, weights=w, seed=seed)
+                      capacity=math.ceil(1.0 * T * K / E), top_experts=top, weights=w, logits=logits, seed=seed)
         return _finish(rng, wl, with_rows)
     raise ValueError(f"unknown workload {cid}")
 
