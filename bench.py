@@ -14,7 +14,8 @@ route_prep and compaction included); ``roofline`` is the dominant kernel's
 algorithmic bytes / its average duration (HIP events on its stream);
 ``cpu_baseline`` is the CPU oracle on the same workload. ``backward`` times,
 outside the step, the backward of the combine fused with wgrad on the same
-buffers (dy in the expert layout + the routing-weight gradient).
+buffers (dy in the expert layout + the routing-weight gradient), and the
+router top-k gating (softmax, renormalised) of the workload's router scores.
 
 Algorithmic bytes per launch (s = element bytes, U = tokens with a kept
 route, N = kept assignments, R = expert-tensor rows):
@@ -22,6 +23,7 @@ route, N = kept assignments, R = expert-tensor rows):
   combine = N*H*s + T*H*s + 8*T*K
   wgrad   = N*H*s + U*H*s + 8*T*K
   combine backward = N*H*s (y) + U*H*s (dout) + R*H*s (dy) + 12*T*K
+  router gating    = 4*T*E (f32 scores) + 8*T*K (experts + weights)
 """
 import argparse
 import ctypes
@@ -76,6 +78,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
+    ap.add_argument("--no-router", action="store_true", help="skip timing the router gating")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device-to-device copies (reference for the HBM byte counters) and exit")
     return ap.parse_args()
@@ -190,20 +193,29 @@ class Step:
                                 P(self.bin_ids), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.wg),
                                 P(self.ws), wsb, st))
         self.order = list(self.calls)
-        # not part of the step: the backward of the combine, dout = grad
+        # not part of the step, timed alone: the backward of the combine
+        # (dout = grad) and the router gating of the workload's scores
+        self.extras = {}
         if self.dy is not None:
-            self.backward = (lib.peg_combine_backward,
-                             (P(self.y), P(self.grad), P(self.w), wl.dtype, wl.layout, T, H, K, E, cap,
-                              P(self.indices), P(self.bin_ids), P(self.bins), P(self.padded_bins), P(self.slot_row),
-                              P(self.dy), self.R, P(self.wg_b), P(self.ws), wsb, st))
+            self.extras["combine_backward"] = (
+                lib.peg_combine_backward,
+                (P(self.y), P(self.grad), P(self.w), wl.dtype, wl.layout, T, H, K, E, cap, P(self.indices),
+                 P(self.bin_ids), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.dy), self.R,
+                 P(self.wg_b), P(self.ws), wsb, st))
+        if wl.logits is not None and not host.get("no_router"):
+            self.logits = host["logits"].to(dev)
+            self.r_top = torch.empty((T, K), **i32)
+            self.r_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+            self.extras["router_topk"] = (lib.peg_router_topk, (P(self.logits), 0, T, E, K, 0, 1, P(self.r_top),
+                                                                P(self.r_w), st))
 
-    def run_backward(self, ev=None, hip=None):
-        fn, args = self.backward
+    def run_extra(self, name, ev=None, hip=None):
+        fn, args = self.extras[name]
         if ev is not None:
             hip.record(ev[0], self.stream)
         rc = fn(*args)
         if rc != 0:
-            raise RuntimeError(f"combine_backward failed with status {rc}")
+            raise RuntimeError(f"{name} failed with status {rc}")
         if ev is not None:
             hip.record(ev[1], self.stream)
 
@@ -225,6 +237,8 @@ def host_inputs(torch, W, wl, peg, dev):
         return torch.from_numpy(a.view("int16")).view(torch.bfloat16 if wl.dtype == W.BF16 else torch.float16)
     conv = (lambda a: torch.from_numpy(a)) if wl.dtype == W.F32 else t16
     host = {"x": conv(wl.x), "grad": conv(wl.grad)}
+    if wl.logits is not None:
+        host["logits"] = torch.from_numpy(wl.logits)
     if wl.routing_map is not None:
         host["probs"] = torch.from_numpy(wl.probs)
         host["rmap"] = torch.from_numpy(wl.routing_map)
@@ -331,6 +345,7 @@ def main():
     ab = algorithmic_bytes(wl, sz, s)
     bytes_step = sum(ab.values())
     host["no_backward"] = args.no_backward
+    host["no_router"] = args.no_router
     per_set = (wl.T * wl.H * s) * 3 + sz["R"] * wl.H * s * (1 if args.no_backward else 2)
     sets = args.sets or max(2, min(16, math.ceil(2 * 2 ** 30 / per_set)))
     log(f"R={sz['R']} N={sz['N']} U={sz['U']} step bytes={bytes_step / 1e6:.1f} MB, {sets} input copies")
@@ -381,25 +396,30 @@ def main():
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic_for(dominant, wl.name),
                     "bytes_per_launch": ab[dominant], "avg_us": kernels[dominant]["avg_us"]}
-    # Timed region 3 (outside the step): the fused combine backward alone, one
+    # Timed region 3 (outside the step): each extra operation alone, one
     # launch per input copy in turn, a HIP event pair around each launch.
-    backward = None
-    if not args.no_backward:
+    extras = {}
+    extra_bytes = {"combine_backward": backward_bytes(wl, sz, s),
+                   "router_topk": wl.T * wl.E * 4 + wl.T * wl.K * 8}
+    for name in steps_obj[0].extras:
         hip = HipEvents()
-        bb = backward_bytes(wl, sz, s)
         for i in range(max(2, args.warmup)):
-            steps_obj[i % sets].run_backward()
+            steps_obj[i % sets].run_extra(name)
         torch.cuda.synchronize()
         bevs = [(hip.create(), hip.create()) for _ in range(args.steps)]
         for i in range(args.steps):
-            steps_obj[i % sets].run_backward(bevs[i], hip)
+            steps_obj[i % sets].run_extra(name, bevs[i], hip)
         torch.cuda.synchronize()
         ms = [hip.elapsed_ms(a, b) for a, b in bevs]
         avg = sum(ms) / len(ms)
-        backward = {"kernel": "combine_backward", "avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
-                    "bytes": bb, "GBps": round(bb / (avg / 1e3) / 1e9, 1),
-                    "frac_peak": round(bb / (avg / 1e3) / 1e9 / PEAK_GBS, 4),
-                    "traffic": traffic_for("backward", wl.name)}
+        bb = extra_bytes[name]
+        extras[name] = {"avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2), "bytes": bb,
+                        "GBps": round(bb / (avg / 1e3) / 1e9, 1),
+                        "frac_peak": round(bb / (avg / 1e3) / 1e9 / PEAK_GBS, 4)}
+        if name == "combine_backward":
+            extras[name]["traffic"] = traffic_for("backward", wl.name)
+        if name == "router_topk":
+            extras[name]["tokens_per_s"] = round(wl.T / (avg / 1e3), 1)
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -422,7 +442,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "backward": backward,
+        "outside_step": extras,
         "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},
     }
     print(json.dumps(line), flush=True)

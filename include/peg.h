@@ -13,7 +13,8 @@
  *   [MOK]  "core.transformer.moe.megakernel.mok.route_adapter" (Megatron-Core
  *          API page): RoutingMapToIndices, routing_map_to_mok_inputs.
  *   [FMD]  "Fused MoE Dispatch (Triton, universal)": the pipeline diagram
- *          (permute ... unpermute + weighted combine).
+ *          (router scores, top-k gating, permute ... unpermute + weighted
+ *          combine) and Usage (gating "softmax" or "sigmoid").
  *
  * Conventions shared by every call
  *   - T tokens, H hidden size, E experts, K = TOP_K routes per token.
@@ -237,6 +238,38 @@ peg_status peg_combine_backward(const void* y, const void* dout, const float* we
                                 const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
                                 const int32_t* padded_bins, const int32_t* slot_row, void* dy, int64_t dy_rows,
                                 float* wgrad, void* ws, size_t ws_bytes, void* stream);
+
+/* Gating functions of peg_router_topk. */
+#define PEG_GATING_SOFTMAX 0
+#define PEG_GATING_SIGMOID 1
+
+/*
+ * peg_router_topk - router top-k gating: scores -> top_experts and weights,
+ * the inputs of peg_route_prep and of the weighted combine.
+ * [FMD] pipeline diagram (router scores -> top-k gating -> permute) and
+ * Usage (gating softmax or sigmoid).
+ *
+ * For each token t, with scores l = logits[t, 0..E-1]:
+ *   top_experts[t, 0..K-1] = the K experts of highest score, highest first;
+ *     equal scores: the lower expert id first; NaN ranks below every
+ *     number; -0 and +0 are equal. The selection is exact (no rounding
+ *     takes part in it).
+ *   p = exp(l - max l) / sum_e exp(l_e - max l) over all E experts
+ *     (PEG_GATING_SOFTMAX) or 1 / (1 + exp(-l)) (PEG_GATING_SIGMOID);
+ *   weights[t, k] = p of expert top_experts[t, k], divided by the sum of the
+ *     K chosen p when normalize != 0. fp32 arithmetic; NaN or infinite
+ *     scores give what those formulas give in IEEE arithmetic. Renormalised
+ *     sigmoid weights stay finite for any finite scores (the common factor
+ *     exp(max l) is cancelled when max l < 0); an unnormalised p below about
+ *     1e-38 may come back as 0.
+ *   logits [T, E] of dtype (PEG_F32, PEG_BF16 or PEG_F16);
+ *   top_experts [T, K] int32 and weights [T, K] f32, fully written.
+ * Errors: NULL_ARG, BAD_SHAPE (T < 0, E < 1, E > PEG_MAX_EXPERTS, K < 1,
+ * K > E, T*E >= 2^31), BAD_DTYPE (also an unknown gating), ALIGNMENT, LAUNCH.
+ */
+peg_status peg_router_topk(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,
+                           int32_t gating, int32_t normalize, int32_t* top_experts, float* weights,
+                           void* stream);
 
 /*
  * peg_routing_map_compact - dense routing map -> fixed-width routes.

@@ -552,7 +552,10 @@ static int score_above(double a, double b) {
  *   - normalize != 0: the K weights are p / (sum of the K selected p), the
  *     renormalisation the workloads' router uses; else the K weights are p.
  * Everything is evaluated in double in that order and rounded once to
- * float32; NaN or infinite scores give whatever those formulas give.
+ * float32; NaN or infinite scores give whatever those formulas give. Domain:
+ * for sigmoid, finite scores above -700 (below that exp(-l) overflows double
+ * and the renormalised weights would become 0/0 instead of their finite
+ * value).
  * gating: 0 = softmax, 1 = sigmoid.
  */
 int pego_router_topk(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,

@@ -8,8 +8,8 @@ without a GPU the calls raise.
 
 Functions (same names as the C entry points without the ``peg_`` prefix):
   route_prep, gather_binned, gather_padded, scatter_combine, wgrad,
-  combine_backward, routing_map_compact, routing_map_compact_backward,
-  validate_routing.
+  combine_backward, router_topk, routing_map_compact,
+  routing_map_compact_backward, validate_routing.
 """
 import ctypes
 import os
@@ -29,6 +29,7 @@ FLAG_BIN_IDS = 0x4
 FLAG_PADDED_BINS = 0x8
 FLAG_INDICES = 0x10
 FLAG_OUT_ROWS = 0x20
+SOFTMAX, SIGMOID = 0, 1
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 _lib = None
@@ -64,6 +65,7 @@ def _load():
                        c_size_t, P], st),
         "peg_combine_backward": ([P, P, P, c_int32, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, P, P, P, P,
                                   P, P, c_int64, P, P, c_size_t, P], st),
+        "peg_router_topk": ([P, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, P, P, P], st),
         "peg_routing_map_compact": ([P, c_int32, P, c_int64, c_int32, c_int32, P, P, P], st),
         "peg_routing_map_compact_backward": ([P, P, c_int64, c_int32, c_int32, P, P], st),
         "peg_validate_routing": ([P, P, P, P, c_int64, c_int32, c_int32, c_int64, P, P, c_size_t, P], st),
@@ -301,6 +303,30 @@ def combine_backward(y, dout, r, weights=None, dy=None, dy_rows=None, wgrad_out=
                                           dy.shape[0], _ptr(wgrad_out), _ptr(ws), wsb, _stream(y.device))
     _check(st, "combine_backward")
     return dy, wgrad_out
+
+
+def router_topk(logits, K, gating=SOFTMAX, normalize=True, top_experts=None, weights=None):
+    """Router top-k gating over scores [T, E] (f32/bf16/f16): returns
+    (top_experts int32 [T, K], highest score first, lower id first on ties;
+    weights f32 [T, K], softmax or sigmoid, renormalised over K if asked)."""
+    logits = _dev(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    if top_experts is None:
+        top_experts = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _dev(top_experts, "top_experts", torch.int32)
+    _dev(weights, "weights", torch.float32)
+    if top_experts.numel() != T * K or weights.numel() != T * K:
+        raise ValueError("top_experts and weights must hold T*K values")
+    with torch.cuda.device(logits.device):
+        st = _load().peg_router_topk(_ptr(logits), _dtype_code(logits, "logits"), T, E, int(K), int(gating),
+                                     1 if normalize else 0, _ptr(top_experts), _ptr(weights),
+                                     _stream(logits.device))
+    _check(st, "router_topk")
+    return top_experts, weights
 
 
 def routing_map_compact(probs, routing_map, topk, probs_out=None, route_experts=None):

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), name
 
@@ -137,6 +137,29 @@ def test_combine_wgrad_checks(lib):
     assert wgr(out=None) == NULL_ARG
     assert wgr(H=-3) == BAD_SHAPE
     assert wgr(g=_p(FAKE + 1)) == ALIGNMENT
+
+
+def test_router_topk_checks(lib):
+    f = lib.peg_router_topk
+
+    def call(lg=_p(FAKE), dt=0, T=4, E=8, K=2, gating=0, norm=1, top=_p(FAKE), w=_p(FAKE)):
+        return f(lg, dt, T, E, K, gating, norm, top, w, None)
+
+    assert call(dt=7) == BAD_DTYPE
+    assert call(gating=2) == BAD_DTYPE
+    assert call(T=-1) == BAD_SHAPE
+    assert call(E=0) == BAD_SHAPE
+    assert call(E=1025, K=2) == BAD_SHAPE
+    assert call(K=0) == BAD_SHAPE
+    assert call(K=9) == BAD_SHAPE                      # K > E
+    assert call(T=1 << 28, E=16) == BAD_SHAPE          # T*E >= 2^31
+    assert call(lg=None) == NULL_ARG
+    assert call(top=None) == NULL_ARG
+    assert call(w=None) == NULL_ARG
+    assert call(lg=_p(FAKE + 2)) == ALIGNMENT          # f32 scores need 4-byte alignment
+    assert call(dt=1, lg=_p(FAKE + 1)) == ALIGNMENT
+    assert call(w=_p(FAKE + 2)) == ALIGNMENT
+    assert call(T=0, lg=None, top=None, w=None) == OK   # nothing to do, nothing enqueued
 
 
 def test_compaction_and_validate_checks(lib):
