@@ -197,21 +197,57 @@ __device__ __forceinline__ uint64_t lanes_below() {
     return (uint64_t(1) << lane_id()) - 1;  // lane 0 -> 0
 }
 
+// DPP lane moves (VALU operations, no LDS crossbar). Lanes whose source is
+// outside the pattern, or whose row is not in ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_read(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_read_f(float v) {
+    return __int_as_float(dpp_read<CTRL>(__float_as_int(v)));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShr = 0x110;     // + n: lane i <- lane i-n of its 16-lane row
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i of its 8 lanes
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i of its row
+constexpr int kDppBcast15 = 0x142;    // rows 1..3 <- last lane of the row before
+constexpr int kDppBcast31 = 0x143;    // rows 2..3 <- lane 31
+
+// Sum over the wave, the same value in every lane: a butterfly inside each
+// 16-lane row (each step adds a pair of partial sums that the two lanes hold
+// in swapped order, so the row's lanes agree), then the four row sums read
+// as scalars and added in row order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    v += dpp_read_f<kDppQuadXor1>(v);
+    v += dpp_read_f<kDppQuadXor2>(v);
+    v += dpp_read_f<kDppHalfMirror>(v);
+    v += dpp_read_f<kDppRowMirror>(v);
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return ((r0 + r1) + r2) + r3;
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside each row by
+// DPP row shifts, then the row totals carried forward by the two row
+// broadcasts). The last lane holds the wave total.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += dpp_read<kDppRowShr + 1>(v);
+    v += dpp_read<kDppRowShr + 2>(v);
+    v += dpp_read<kDppRowShr + 4>(v);
+    v += dpp_read<kDppRowShr + 8>(v);
+    v += dpp_read<kDppBcast15, 0xA>(v);
+    v += dpp_read<kDppBcast31, 0xC>(v);
     return v;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int y = __shfl_up(v, d, kWave);
-        if (lane >= d) v += y;
-    }
-    return v;
-}
+// Value of lane 63 in every lane.
+__device__ __forceinline__ int last_lane(int v) { return __builtin_amdgcn_readlane(v, kWave - 1); }
 
 // Exclusive prefix sum over the NT threads of a block (NT a multiple of 64).
 // `scratch` holds NT/64 ints of LDS. Returns the prefix of this thread's

@@ -60,7 +60,7 @@ __device__ __forceinline__ void scan_chunks(int* cnt, int nch, int E, int* tot) 
                 const int v = c < nch ? cnt[c * E + e] : 0;
                 const int inc = wave_inclusive_scan(v);
                 if (c < nch) cnt[c * E + e] = carry + inc - v;
-                carry += __shfl(inc, kWave - 1, kWave);
+                carry += last_lane(inc);
             }
             if (tot && lane == 0) tot[e] = carry;
         }

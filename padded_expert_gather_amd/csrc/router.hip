@@ -43,31 +43,20 @@ __device__ __forceinline__ float key_score(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// One DPP lane move of a 32-bit value (every source lane is inside the
-// caller's group, so no lane reads outside it).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
-constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
-
 template <int CTRL>
 __device__ __forceinline__ uint64_t max_step(uint64_t v) {
-    const uint64_t o = ((uint64_t)dpp_move<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_move<CTRL>((uint32_t)v);
+    const uint64_t o = ((uint64_t)(uint32_t)dpp_read<CTRL>((int)(v >> 32)) << 32) |
+                       (uint32_t)dpp_read<CTRL>((int)(uint32_t)v);
     return o > v ? o : v;
 }
 
 // Maximum over the G lanes of a group; every lane of it gets the result.
 template <int G>
 __device__ __forceinline__ uint64_t group_max(uint64_t v) {
-    v = max_step<kDppXor1>(v);
-    v = max_step<kDppXor2>(v);
+    v = max_step<kDppQuadXor1>(v);
+    v = max_step<kDppQuadXor2>(v);
     v = max_step<kDppHalfMirror>(v);
-    if constexpr (G >= 16) v = max_step<kDppMirror>(v);
+    if constexpr (G >= 16) v = max_step<kDppRowMirror>(v);
 #pragma unroll
     for (int d = 16; d < G; d <<= 1) {
         const uint64_t o = __shfl_xor(v, d, G);
@@ -76,20 +65,15 @@ __device__ __forceinline__ uint64_t group_max(uint64_t v) {
     return v;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float add_step(float v) {
-    return v + __uint_as_float(dpp_move<CTRL>(__float_as_uint(v)));
-}
-
 // Sum over the G lanes of a group, the same value in every lane (each step
 // adds two partial sums that the pair of lanes holds in swapped order, and
 // float addition is commutative).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-    v = add_step<kDppXor1>(v);
-    v = add_step<kDppXor2>(v);
-    v = add_step<kDppHalfMirror>(v);
-    if constexpr (G >= 16) v = add_step<kDppMirror>(v);
+    v += dpp_read_f<kDppQuadXor1>(v);
+    v += dpp_read_f<kDppQuadXor2>(v);
+    v += dpp_read_f<kDppHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp_read_f<kDppRowMirror>(v);
 #pragma unroll
     for (int d = 16; d < G; d <<= 1) v += __shfl_xor(v, d, G);
     return v;
