@@ -15,7 +15,8 @@ algorithmic bytes / its average duration (HIP events on its stream);
 ``cpu_baseline`` is the CPU oracle on the same workload. ``backward`` times,
 outside the step, the backward of the combine fused with wgrad on the same
 buffers (dy in the expert layout + the routing-weight gradient), and the
-router top-k gating (softmax, renormalised) of the workload's router scores.
+router top-k gating (softmax, renormalised) of the workload's router scores,
+alone and fused with route_prep.
 
 Algorithmic bytes per launch (s = element bytes, U = tokens with a kept
 route, N = kept assignments, R = expert-tensor rows):
@@ -208,6 +209,19 @@ class Step:
             self.r_w = torch.empty((T, K), dtype=torch.float32, device=dev)
             self.extras["router_topk"] = (lib.peg_router_topk, (P(self.logits), 0, T, E, K, 0, 1, P(self.r_top),
                                                                 P(self.r_w), st))
+            # gating fused with route_prep, into buffers of its own
+            self.f_idx = torch.empty(total, **i32)
+            self.f_bid = torch.empty(total, **i32)
+            self.f_tpe = torch.empty(E, **i32)
+            self.f_bins = torch.empty(E, **i32)
+            self.f_pb = torch.empty(E, **i32) if wl.layout == W.PADDED else None
+            self.f_slot = torch.empty(total, **i32)
+            self.f_ws = torch.empty(peg.workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)
+            self.extras["route_prep_logits"] = (
+                lib.peg_route_prep_logits,
+                (P(self.logits), 0, T, E, K, 0, 1, wl.layout, cap, m, P(self.r_top), P(self.r_w), P(self.f_idx),
+                 P(self.f_bid), P(self.f_tpe), P(self.f_bins), P(self.f_pb), P(self.f_slot), P(self.f_ws),
+                 self.f_ws.numel(), st))
 
     def run_extra(self, name, ev=None, hip=None):
         fn, args = self.extras[name]
@@ -400,7 +414,8 @@ def main():
     # launch per input copy in turn, a HIP event pair around each launch.
     extras = {}
     extra_bytes = {"combine_backward": backward_bytes(wl, sz, s),
-                   "router_topk": wl.T * wl.E * 4 + wl.T * wl.K * 8}
+                   "router_topk": wl.T * wl.E * 4 + wl.T * wl.K * 8,
+                   "route_prep_logits": wl.T * wl.E * 4 + wl.T * wl.K * 8 + 16 * wl.T * wl.K}
     for name in steps_obj[0].extras:
         hip = HipEvents()
         for i in range(max(2, args.warmup)):
@@ -418,7 +433,7 @@ def main():
                         "frac_peak": round(bb / (avg / 1e3) / 1e9 / PEAK_GBS, 4)}
         if name == "combine_backward":
             extras[name]["traffic"] = traffic_for("backward", wl.name)
-        if name == "router_topk":
+        if name in ("router_topk", "route_prep_logits"):
             extras[name]["tokens_per_s"] = round(wl.T / (avg / 1e3), 1)
     cpu = None
     if not args.no_cpu:

@@ -272,6 +272,30 @@ peg_status peg_router_topk(const void* logits, int32_t dtype, int64_t T, int32_t
                            void* stream);
 
 /*
+ * peg_route_prep_logits - router top-k gating fused with the routing
+ * preparation: one call from router scores to everything peg_route_prep
+ * writes. [FMD] pipeline diagram (router scores -> top-k gating -> permute)
+ * and [PAD]/[BIN] Workflow steps 1-3.
+ *
+ * Writes top_experts [T, K] and weights [T, K] exactly as peg_router_topk
+ * does, and indices, bin_ids, tokens_per_expert, bins, padded_bins and
+ * slot_row exactly as peg_route_prep(top_experts, ...) does. The gating pass
+ * also counts the experts of each tile of assignment ids, so no separate
+ * histogram pass reads top_experts back.
+ *   Arguments: those of peg_router_topk, then those of peg_route_prep after
+ *   its top_experts (layout, capacity, pad_multiple, indices, bin_ids,
+ *   tokens_per_expert, bins, padded_bins, slot_row, ws, ws_bytes).
+ *   ws: at least peg_workspace_bytes(T, K, E).
+ * Errors: those of both calls.
+ */
+peg_status peg_route_prep_logits(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,
+                                 int32_t gating, int32_t normalize, int32_t layout, int32_t capacity,
+                                 int32_t pad_multiple, int32_t* top_experts, float* weights,
+                                 int32_t* indices, int32_t* bin_ids, int32_t* tokens_per_expert,
+                                 int32_t* bins, int32_t* padded_bins, int32_t* slot_row, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * peg_routing_map_compact - dense routing map -> fixed-width routes.
  * [MOK] RoutingMapToIndices and routing_map_to_mok_inputs.
  *

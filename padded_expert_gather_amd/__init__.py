@@ -8,7 +8,7 @@ without a GPU the calls raise.
 
 Functions (same names as the C entry points without the ``peg_`` prefix):
   route_prep, gather_binned, gather_padded, scatter_combine, wgrad,
-  combine_backward, router_topk, routing_map_compact,
+  combine_backward, router_topk, route_prep_logits, routing_map_compact,
   routing_map_compact_backward, validate_routing.
 """
 import ctypes
@@ -66,6 +66,8 @@ def _load():
         "peg_combine_backward": ([P, P, P, c_int32, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, P, P, P, P,
                                   P, P, c_int64, P, P, c_size_t, P], st),
         "peg_router_topk": ([P, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, P, P, P], st),
+        "peg_route_prep_logits": ([P, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                   c_int32, P, P, P, P, P, P, P, P, P, c_size_t, P], st),
         "peg_routing_map_compact": ([P, c_int32, P, c_int64, c_int32, c_int32, P, P, P], st),
         "peg_routing_map_compact_backward": ([P, P, c_int64, c_int32, c_int32, P, P], st),
         "peg_validate_routing": ([P, P, P, P, c_int64, c_int32, c_int32, c_int64, P, P, c_size_t, P], st),
@@ -178,6 +180,40 @@ def route_prep(top_experts, num_experts, capacity=None, pad_multiple=None, ws=No
                                     _ptr(slot_row), _ptr(ws), wsb, _stream(dev))
     _check(st, "route_prep")
     return Routing(T, K, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins, padded, slot_row)
+
+
+def route_prep_logits(logits, K, capacity=None, pad_multiple=None, gating=SOFTMAX, normalize=True, ws=None):
+    """Router top-k gating fused with route_prep: router scores [T, E]
+    (f32/bf16/f16) -> (Routing, top_experts int32 [T, K], weights f32 [T, K]).
+    Same layouts as :func:`route_prep`."""
+    logits = _dev(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    K = int(K)
+    if capacity is None and pad_multiple is None:
+        raise ValueError("give capacity (binned) or pad_multiple (padded)")
+    layout = BINNED if capacity is not None else PADDED
+    dev = logits.device
+    total = T * K
+    i32 = dict(dtype=torch.int32, device=dev)
+    top = torch.empty((T, K), **i32)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    indices = torch.empty(total, **i32)
+    bin_ids = torch.empty(total, **i32)
+    tpe = torch.empty(E, **i32)
+    bins = torch.empty(E, **i32)
+    padded = torch.empty(E, **i32) if pad_multiple is not None else None
+    slot_row = torch.empty(total, **i32)
+    ws, wsb = _ws(T, K, E, dev, ws)
+    with torch.cuda.device(dev):
+        st = _load().peg_route_prep_logits(_ptr(logits), _dtype_code(logits, "logits"), T, E, K, int(gating),
+                                           1 if normalize else 0, layout, int(capacity or 0),
+                                           int(pad_multiple or 0), _ptr(top), _ptr(w), _ptr(indices),
+                                           _ptr(bin_ids), _ptr(tpe), _ptr(bins), _ptr(padded), _ptr(slot_row),
+                                           _ptr(ws), wsb, _stream(dev))
+    _check(st, "route_prep_logits")
+    return Routing(T, K, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins, padded, slot_row), top, w
 
 
 def _slot(r, use_slot_row):

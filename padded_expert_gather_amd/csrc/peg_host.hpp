@@ -80,9 +80,21 @@ inline int64_t token_blocks(int64_t T, int wpt) {
 // Tiles of the routing preparation: 256 threads x ITEMS assignments. The
 // per-chunk count table of a tile (4 * ITEMS chunks of 64 x E ints) stays
 // within 32 KB of LDS.
+// Small inputs take fewer ids per thread (down to 1) until they make at least
+// kMinTiles tiles, so that more CUs share the work.
+#ifndef PEG_MIN_TILES
+#define PEG_MIN_TILES 32
+#endif
 inline int prep_items(int32_t E) { return E <= 128 ? 16 : (E <= 256 ? 8 : (E <= 512 ? 4 : 2)); }
-inline int64_t prep_tile(int32_t E) { return (int64_t)kBlock * prep_items(E); }
-inline int64_t prep_tiles(int64_t total, int32_t E) { return (total + prep_tile(E) - 1) / prep_tile(E); }
+inline int64_t tiles_of(int64_t total, int items) {
+    return (total + (int64_t)kBlock * items - 1) / ((int64_t)kBlock * items);
+}
+inline int tiled_items(int64_t total, int32_t E) {
+    int items = prep_items(E);
+    while (items > 1 && tiles_of(total, items) < PEG_MIN_TILES) items >>= 1;
+    return items;
+}
+inline int64_t prep_tiles(int64_t total, int32_t E) { return tiles_of(total, tiled_items(total, E)); }
 
 // Workspace: every call uses one region starting at offset 0.
 inline size_t ws_need(int64_t T, int32_t K, int32_t E) {
@@ -118,6 +130,15 @@ inline peg_status launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
 
 // Rebuilds the assignment -> row map from the sorted routing arrays into the
 // workspace (internal; shared by the gathers, the combine and wgrad).
+// Placement of the routing preparation from per-tile expert counts
+// (counts[e * ntiles + tile], tiles of kBlock * items ids, items one of
+// 1, 2, 4, 8, 16): writes indices, bin_ids, tokens_per_expert, bins,
+// padded_bins (if non-NULL) and slot_row (if non-NULL). Defined in
+// route_prep.hip.
+peg_status prep_place(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                      int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                      int32_t* padded_bins, int32_t* slot_row, int32_t* counts, int items, hipStream_t s);
+
 peg_status rebuild_slot_row(int64_t total, int32_t E, int32_t layout, int32_t capacity,
                             const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
                             const int32_t* padded_bins, int32_t* slot_row, hipStream_t s);

@@ -16,9 +16,10 @@
 // result is deterministic.
 //
 // Paths:
-//   small: T*K <= 16384 and its count table fits in LDS -> one 1024-thread
+//   small: T*K < 8192 and its count table fits in LDS -> one 1024-thread
 //          block does everything (histogram, scans, placement) in one launch;
-//   tiled: tiles of 256*ITEMS ids; a histogram launch, then a placement
+//   tiled: tiles of 256*ITEMS ids (ITEMS shrinks for small inputs so that
+//          there are at least 32 tiles); a histogram launch, then a placement
 //          launch in which every block reads the (experts x tiles) count
 //          table and derives its own bases (block 0 also writes the bins);
 //          when that table is large, a single-block scan launch in between
@@ -89,7 +90,13 @@ __device__ __forceinline__ int position_row(int layout, int e, int capacity, int
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
-constexpr int64_t kSmallMaxIds = 16384;
+// Inputs of at least kBlock * PEG_MIN_TILES ids (32 tiles of 256) go to the
+// tiled path: two launches over 32+ CUs beat one CU from there on (measured
+// 7.7 vs 8.9 us at 8192 ids).
+#ifndef PEG_SMALL_MAX_IDS
+#define PEG_SMALL_MAX_IDS (kBlock * PEG_MIN_TILES - 1)
+#endif
+constexpr int64_t kSmallMaxIds = PEG_SMALL_MAX_IDS;
 constexpr size_t kSmallMaxTable = 48 * 1024;
 constexpr size_t kSmallMaxLds = 64 * 1024 - 512;  // dynamic LDS budget of the small path
 
@@ -415,20 +422,31 @@ static int id_bits(int E) {
 constexpr int64_t kMergedMaxTable = 16384;
 
 template <int ITEMS>
-static peg_status prep_tiled(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
-                             int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
-                             int32_t* padded_bins, int32_t* slot_row, int32_t* counts, hipStream_t s) {
-    const int64_t ntiles = (total + (int64_t)kBlock * ITEMS - 1) / ((int64_t)kBlock * ITEMS);
-    PEG_CHECK(launch(tile_hist_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), 0, s, top, total, E, ntiles,
-                     counts));
+static peg_status place_tiles(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                              int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                              int32_t* padded_bins, int32_t* slot_row, int32_t* counts, hipStream_t s) {
+    const int64_t ntiles = tiles_of(total, ITEMS);
     const int32_t merged = ntiles * E <= kMergedMaxTable ? 1 : 0;
     if (!merged || ntiles == 0)
         PEG_CHECK(launch(tile_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E, pad_multiple, tpe,
                          bins, padded_bins));
+    if (ntiles == 0) return PEG_OK;
     const size_t lds = ((size_t)ITEMS * (kBlock / kWave) * E + 3 * (size_t)E) * sizeof(int);
     return launch(tile_place_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,
                   id_bits(E), counts, ntiles, merged ? 0 : 1, pad_multiple, layout, capacity, indices, bin_ids, tpe,
                   bins, padded_bins, slot_row);
+}
+
+template <int ITEMS>
+static peg_status prep_tiled(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                             int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                             int32_t* padded_bins, int32_t* slot_row, int32_t* counts, hipStream_t s) {
+    const int64_t ntiles = tiles_of(total, ITEMS);
+    if (ntiles > 0)
+        PEG_CHECK(launch(tile_hist_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), 0, s, top, total, E, ntiles,
+                         counts));
+    return place_tiles<ITEMS>(top, total, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins,
+                              padded_bins, slot_row, counts, s);
 }
 
 template <int ITEMS>
@@ -489,16 +507,39 @@ PEG_API peg_status peg_route_prep(const int32_t* top_experts, int64_t T, int32_t
         default: break;
     }
     int32_t* counts = reinterpret_cast<int32_t*>(ws);
-    const int items = prep_items(E);
-    if (items == 16)
-        return prep_tiled<16>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                              tokens_per_expert, bins, padded_bins, slot_row, counts, s);
-    if (items == 8)
-        return prep_tiled<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                             tokens_per_expert, bins, padded_bins, slot_row, counts, s);
-    if (items == 4)
-        return prep_tiled<4>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                             tokens_per_expert, bins, padded_bins, slot_row, counts, s);
-    return prep_tiled<2>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                         tokens_per_expert, bins, padded_bins, slot_row, counts, s);
+    switch (tiled_items(total, E)) {
+#define PEG_TILED(I)                                                                                             \
+    case I:                                                                                                      \
+        return prep_tiled<I>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,            \
+                             tokens_per_expert, bins, padded_bins, slot_row, counts, s)
+        PEG_TILED(16);
+        PEG_TILED(8);
+        PEG_TILED(4);
+        PEG_TILED(2);
+        PEG_TILED(1);
+#undef PEG_TILED
+        default: return PEG_ERR_BAD_SHAPE;
+    }
 }
+
+namespace peg {
+
+peg_status prep_place(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                      int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                      int32_t* padded_bins, int32_t* slot_row, int32_t* counts, int items, hipStream_t s) {
+    switch (items) {
+#define PEG_PLACE(I)                                                                                             \
+    case I:                                                                                                      \
+        return place_tiles<I>(top, total, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins,        \
+                              padded_bins, slot_row, counts, s)
+        PEG_PLACE(16);
+        PEG_PLACE(8);
+        PEG_PLACE(4);
+        PEG_PLACE(2);
+        PEG_PLACE(1);
+#undef PEG_PLACE
+        default: return PEG_ERR_BAD_SHAPE;
+    }
+}
+
+}  // namespace peg

@@ -1,5 +1,6 @@
 // router.hip - router top-k gating on gfx950: per-token scores -> the K
-// chosen experts and their weights, the input of route_prep.
+// chosen experts and their weights, the input of route_prep; and the same
+// gating fused with route_prep's histogram pass.
 //
 // Source: "Fused MoE Dispatch (Triton, universal)", the pipeline figure
 // (router scores, then top-k gating, then permute) and Usage (gating by
@@ -85,17 +86,14 @@ __device__ __forceinline__ float load_score(const void* p, int64_t i) {
     else return decode<DT>(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
-// G lanes per token, CPL scores per lane (E <= G * CPL).
+// Gating of token t by the G lanes of a group (lane g): on return, lane g
+// holds the results k = j * G + g (k < K) in sel_e[j] (expert) and sel_w[j]
+// (weight). Every lane of the group must call it.
 template <int DT, int G, int CPL>
-__global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restrict__ logits, int64_t T, int32_t E,
-                                                             int32_t K, int32_t gating, int32_t normalize,
-                                                             int32_t* __restrict__ top_experts,
-                                                             float* __restrict__ weights) {
+__device__ __forceinline__ void gate_token(const void* __restrict__ logits, int64_t t, int32_t E, int32_t K,
+                                           int32_t gating, int32_t normalize, int g, int32_t (&sel_e)[CPL],
+                                           float (&sel_w)[CPL]) {
     static_assert(G >= 8 && G <= kWave && (G & (G - 1)) == 0, "group of 8..64 lanes");
-    constexpr int TPB = kBlock / G;
-    const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
-    if (t >= T) return;  // whole groups leave together: reductions stay within live groups
-    const int g = threadIdx.x % G;
     uint64_t key[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -124,12 +122,10 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restr
     // exp(-l) cannot overflow fp32 and turn the weights into 0 / 0.
     const bool shifted = gating != 0 && normalize && m < 0.0f;
     // K selection rounds; result k lands in slot k / G of lane k % G.
-    int32_t sel_e[CPL];
-    float sel_p[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         sel_e[j] = 0;
-        sel_p[j] = 0.0f;
+        sel_w[j] = 0.0f;
     }
     for (int k = 0; k < K; ++k) {
         uint64_t best = 0;
@@ -152,48 +148,142 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restr
             for (int j = 0; j < CPL; ++j)
                 if (j == k / G) {
                     sel_e[j] = e;
-                    sel_p[j] = p;
+                    sel_w[j] = p;
                 }
         }
     }
-    float sel_sum = 0.0f;
     if (normalize) {
+        float sel_sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) sel_sum += sel_p[j];  // slots past K hold 0
+        for (int j = 0; j < CPL; ++j) sel_sum += sel_w[j];  // slots past K hold 0
         sel_sum = group_sum<G>(sel_sum);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) sel_w[j] = sel_w[j] / sel_sum;
     }
+}
+
+// G lanes per token, CPL scores per lane (E <= G * CPL).
+template <int DT, int G, int CPL>
+__global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restrict__ logits, int64_t T, int32_t E,
+                                                             int32_t K, int32_t gating, int32_t normalize,
+                                                             int32_t* __restrict__ top_experts,
+                                                             float* __restrict__ weights) {
+    constexpr int TPB = kBlock / G;
+    const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
+    if (t >= T) return;  // whole groups leave together: reductions stay within live groups
+    const int g = threadIdx.x % G;
+    int32_t sel_e[CPL];
+    float sel_w[CPL];
+    gate_token<DT, G, CPL>(logits, t, E, K, gating, normalize, g, sel_e, sel_w);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int k = j * G + g;
         if (k < K) {
             top_experts[t * K + k] = sel_e[j];
-            weights[t * K + k] = normalize ? sel_p[j] / sel_sum : sel_p[j];
+            weights[t * K + k] = sel_w[j];
         }
     }
 }
 
+// Gating fused with the first pass of the routing preparation: block b owns
+// the assignment ids [b * tile, (b + 1) * tile) and gates every token that
+// has an id there (a token that straddles two tiles is gated by both blocks,
+// identically; the block holding its first id writes its outputs). The
+// block's expert histogram of its ids goes to counts[e * ntiles + b], the
+// table the placement pass reads.
+constexpr int kHistThreads = 1024;  // gating lanes of a tile: 128 tokens per pass at 8 lanes per token
+
 template <int DT, int G, int CPL>
-static peg_status router_go(hipStream_t s, const void* logits, int64_t T, int32_t E, int32_t K, int32_t gating,
-                            int32_t normalize, int32_t* top, float* w) {
+__global__ __launch_bounds__(kHistThreads) void router_hist_kernel(const void* __restrict__ logits, int64_t T, int32_t E,
+                                                             int32_t K, int32_t gating, int32_t normalize,
+                                                             int64_t tile, int64_t ntiles,
+                                                             int32_t* __restrict__ top_experts,
+                                                             float* __restrict__ weights,
+                                                             int32_t* __restrict__ counts) {
+    constexpr int TPB = kHistThreads / G;
+    __shared__ int hist[PEG_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += kHistThreads) hist[e] = 0;
+    lds_barrier();
+    const int64_t total = T * (int64_t)K;
+    const int64_t lo = (int64_t)blockIdx.x * tile;
+    const int64_t hi = lo + tile < total ? lo + tile : total;
+    const int64_t t_first = lo / K;
+    const int64_t t_last = (hi - 1) / K;  // hi > lo: every launched tile holds an id
+    const int g = threadIdx.x % G;
+    for (int64_t t0 = t_first; t0 <= t_last; t0 += TPB) {
+        const int64_t t = t0 + threadIdx.x / G;
+        if (t > t_last) continue;  // whole groups skip together
+        int32_t sel_e[CPL];
+        float sel_w[CPL];
+        gate_token<DT, G, CPL>(logits, t, E, K, gating, normalize, g, sel_e, sel_w);
+        const bool owner = t * K >= lo;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int k = j * G + g;
+            if (k < K) {
+                const int64_t a = t * K + k;
+                if (a >= lo && a < hi) atomicAdd(&hist[sel_e[j]], 1);
+                if (owner) {
+                    top_experts[a] = sel_e[j];
+                    weights[a] = sel_w[j];
+                }
+            }
+        }
+    }
+    lds_barrier();
+    for (int e = threadIdx.x; e < E; e += kHistThreads) counts[(int64_t)e * ntiles + blockIdx.x] = hist[e];
+}
+
+// Launch arguments of both gating kernels.
+struct GateArgs {
+    const void* logits;
+    int64_t T;
+    int32_t E, K, gating, normalize;
+    int32_t* top;
+    float* w;
+    int64_t tile, ntiles;  // fused histogram only (ntiles > 0)
+    int32_t* counts;
+};
+
+template <int DT, int G, int CPL>
+static peg_status gate_go(hipStream_t s, const GateArgs& a) {
+    if (a.ntiles > 0)
+        return launch(router_hist_kernel<DT, G, CPL>, dim3((unsigned)a.ntiles), dim3(kHistThreads), 0, s, a.logits, a.T,
+                      a.E, a.K, a.gating, a.normalize, a.tile, a.ntiles, a.top, a.w, a.counts);
     constexpr int TPB = kBlock / G;
-    const dim3 grid((unsigned)((T + TPB - 1) / TPB));
-    return launch(router_topk_kernel<DT, G, CPL>, grid, dim3(kBlock), 0, s, logits, T, E, K, gating, normalize, top,
-                  w);
+    const dim3 grid((unsigned)((a.T + TPB - 1) / TPB));
+    return launch(router_topk_kernel<DT, G, CPL>, grid, dim3(kBlock), 0, s, a.logits, a.T, a.E, a.K, a.gating,
+                  a.normalize, a.top, a.w);
 }
 
 template <int DT>
-static peg_status router_dispatch(hipStream_t s, const void* logits, int64_t T, int32_t E, int32_t K,
-                                  int32_t gating, int32_t normalize, int32_t* top, float* w) {
-#define PEG_ROUTER(GG, CC) return router_go<DT, GG, CC>(s, logits, T, E, K, gating, normalize, top, w)
-    if (E <= 8) PEG_ROUTER(8, 1);
-    if (E <= 16) PEG_ROUTER(8, 2);
-    if (E <= 32) PEG_ROUTER(8, 4);
-    if (E <= 64) PEG_ROUTER(8, 8);
-    if (E <= 128) PEG_ROUTER(8, 16);
-    if (E <= 256) PEG_ROUTER(8, 32);
-    if (E <= 512) PEG_ROUTER(16, 32);
-    PEG_ROUTER(32, 32);
-#undef PEG_ROUTER
+static peg_status gate_dispatch(hipStream_t s, const GateArgs& a) {
+    if (a.E <= 8) return gate_go<DT, 8, 1>(s, a);
+    if (a.E <= 16) return gate_go<DT, 8, 2>(s, a);
+    if (a.E <= 32) return gate_go<DT, 8, 4>(s, a);
+    if (a.E <= 64) return gate_go<DT, 8, 8>(s, a);
+    if (a.E <= 128) return gate_go<DT, 8, 16>(s, a);
+    if (a.E <= 256) return gate_go<DT, 8, 32>(s, a);
+    if (a.E <= 512) return gate_go<DT, 16, 32>(s, a);
+    return gate_go<DT, 32, 32>(s, a);
+}
+
+static peg_status gate(int32_t dtype, hipStream_t s, const GateArgs& a) {
+    if (dtype == PEG_F32) return gate_dispatch<PEG_F32>(s, a);
+    if (dtype == PEG_BF16) return gate_dispatch<PEG_BF16>(s, a);
+    return gate_dispatch<PEG_F16>(s, a);
+}
+
+static peg_status gate_checks(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K, int32_t gating,
+                              const int32_t* top_experts, const float* weights) {
+    if (!dtype_ok(dtype) || (gating != PEG_GATING_SOFTMAX && gating != PEG_GATING_SIGMOID))
+        return PEG_ERR_BAD_DTYPE;
+    if (T < 0 || E < 1 || E > PEG_MAX_EXPERTS || K < 1 || K > E) return PEG_ERR_BAD_SHAPE;
+    if (T > kMaxAssign / E) return PEG_ERR_BAD_SHAPE;
+    if (T > 0 && (!logits || !top_experts || !weights)) return PEG_ERR_NULL_ARG;
+    if (!aligned(logits, elem_bytes(dtype)) || !aligned(top_experts, 4) || !aligned(weights, 4))
+        return PEG_ERR_ALIGNMENT;
+    return PEG_OK;
 }
 
 }  // namespace peg
@@ -203,17 +293,39 @@ using namespace peg;
 PEG_API peg_status peg_router_topk(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,
                                    int32_t gating, int32_t normalize, int32_t* top_experts, float* weights,
                                    void* stream) {
-    if (!dtype_ok(dtype) || (gating != PEG_GATING_SOFTMAX && gating != PEG_GATING_SIGMOID))
-        return PEG_ERR_BAD_DTYPE;
-    if (T < 0 || E < 1 || E > PEG_MAX_EXPERTS || K < 1 || K > E) return PEG_ERR_BAD_SHAPE;
-    if (T > kMaxAssign / E) return PEG_ERR_BAD_SHAPE;
-    if (T > 0 && (!logits || !top_experts || !weights)) return PEG_ERR_NULL_ARG;
-    if (!aligned(logits, elem_bytes(dtype)) || !aligned(top_experts, 4) || !aligned(weights, 4))
-        return PEG_ERR_ALIGNMENT;
+    PEG_CHECK(gate_checks(logits, dtype, T, E, K, gating, top_experts, weights));
     if (T == 0) return PEG_OK;
+    const GateArgs a{logits, T, E, K, gating, normalize ? 1 : 0, top_experts, weights, 0, 0, nullptr};
+    return gate(dtype, reinterpret_cast<hipStream_t>(stream), a);
+}
+
+PEG_API peg_status peg_route_prep_logits(const void* logits, int32_t dtype, int64_t T, int32_t E, int32_t K,
+                                         int32_t gating, int32_t normalize, int32_t layout, int32_t capacity,
+                                         int32_t pad_multiple, int32_t* top_experts, float* weights,
+                                         int32_t* indices, int32_t* bin_ids, int32_t* tokens_per_expert,
+                                         int32_t* bins, int32_t* padded_bins, int32_t* slot_row, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    PEG_CHECK(gate_checks(logits, dtype, T, E, K, gating, top_experts, weights));
+    // the routing-preparation checks of peg_route_prep
+    if (!layout_ok(layout)) return PEG_ERR_BAD_DTYPE;
+    if (T > kMaxAssign / K) return PEG_ERR_BAD_SHAPE;
+    const int64_t total = T * (int64_t)K;
+    if (layout == PEG_BINNED && (capacity < 1 || (int64_t)E * capacity > kMaxAssign)) return PEG_ERR_BAD_SHAPE;
+    const bool need_pad = padded_bins != nullptr || layout == PEG_PADDED;
+    if (need_pad && pad_multiple < 1) return PEG_ERR_BAD_SHAPE;
+    if (need_pad && total + (int64_t)E * (pad_multiple - 1) > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    if (!bins || (total > 0 && (!indices || !bin_ids))) return PEG_ERR_NULL_ARG;
+    if (layout == PEG_PADDED && !padded_bins) return PEG_ERR_NULL_ARG;
+    if (!ws || ws_bytes < ws_need(T, K, E)) return PEG_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int32_t norm = normalize ? 1 : 0;
-    if (dtype == PEG_F32) return router_dispatch<PEG_F32>(s, logits, T, E, K, gating, norm, top_experts, weights);
-    if (dtype == PEG_BF16) return router_dispatch<PEG_BF16>(s, logits, T, E, K, gating, norm, top_experts, weights);
-    return router_dispatch<PEG_F16>(s, logits, T, E, K, gating, norm, top_experts, weights);
+    const int items = tiled_items(total, E);
+    const int64_t ntiles = tiles_of(total, items);
+    int32_t* counts = reinterpret_cast<int32_t*>(ws);
+    if (ntiles > 0) {
+        const GateArgs a{logits, T, E, K, gating, normalize ? 1 : 0, top_experts, weights,
+                         (int64_t)kBlock * items, ntiles, counts};
+        PEG_CHECK(gate(dtype, s, a));
+    }
+    return prep_place(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids, tokens_per_expert,
+                      bins, padded_bins, slot_row, counts, items, s);
 }

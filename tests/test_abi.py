@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
 
@@ -160,6 +160,29 @@ def test_router_topk_checks(lib):
     assert call(dt=1, lg=_p(FAKE + 1)) == ALIGNMENT
     assert call(w=_p(FAKE + 2)) == ALIGNMENT
     assert call(T=0, lg=None, top=None, w=None) == OK   # nothing to do, nothing enqueued
+
+
+def test_route_prep_logits_checks(lib):
+    f = lib.peg_route_prep_logits
+
+    def call(lg=_p(FAKE), dt=0, T=4, E=8, K=2, gating=0, layout=0, C=2, m=0, top=_p(FAKE), w=_p(FAKE),
+             idx=_p(FAKE), bins=_p(FAKE), pb=None, ws=_p(FAKE), wsb=1 << 20):
+        return f(lg, dt, T, E, K, gating, 1, layout, C, m, top, w, idx, _p(FAKE), None, bins, pb, None, ws, wsb,
+                 None)
+
+    assert call(dt=5) == BAD_DTYPE
+    assert call(gating=3) == BAD_DTYPE
+    assert call(layout=4) == BAD_DTYPE
+    assert call(K=9) == BAD_SHAPE
+    assert call(C=0) == BAD_SHAPE                      # binned needs capacity >= 1
+    assert call(layout=1, pb=_p(FAKE), m=0) == BAD_SHAPE
+    assert call(layout=1, m=4, pb=None) == NULL_ARG
+    assert call(idx=None) == NULL_ARG
+    assert call(bins=None) == NULL_ARG
+    assert call(top=None) == NULL_ARG
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=8) == WORKSPACE
+    assert call(w=_p(FAKE + 1)) == ALIGNMENT
 
 
 def test_compaction_and_validate_checks(lib):

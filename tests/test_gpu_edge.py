@@ -69,7 +69,9 @@ CASES = [
     _case("E1024_scan_launch", 10000, 2, 1024, 8, W.BF16, P, m=2),
     _case("E200_merged_bases", 3000, 8, 200, 8, W.BF16, P, m=16, none_frac=0.1),
     _case("E64_tile4096", 9000, 8, 64, 8, W.BF16, B, cap=1000, skew=0.05),
-    _case("small_staged_12k", 6000, 2, 8, 8, W.BF16, P, m=64, none_frac=0.05),
+    _case("tiled_items1_12k", 6000, 2, 8, 8, W.BF16, P, m=64, none_frac=0.05),
+    _case("small_staged_6k", 3000, 2, 8, 8, W.BF16, P, m=64, none_frac=0.05),
+    _case("tiled_8192", 4096, 2, 8, 8, W.BF16, P, m=128),
     _case("small_unstaged", 4000, 2, 64, 8, W.BF16, B, cap=100),
     _case("tile_2048", 1024, 2, 8, 16, W.BF16, B, cap=300),
     _case("tile_2049", 683, 3, 8, 16, W.BF16, P, m=8),

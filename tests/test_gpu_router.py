@@ -127,3 +127,47 @@ def test_router_feeds_route_prep():
     assert np.array_equal(to_host(rg.indices), ro.indices)
     assert np.array_equal(to_host(rg.padded_bins), ro.padded_bins)
     assert math.isclose(float(ro.n), wl.T * wl.K)
+
+
+FUSED = [  # (T, E, K, layout, capacity or multiple, score kind)
+    (0, 8, 2, W.BINNED, 4, "normal"),
+    (1, 8, 2, W.PADDED, 4, "normal"),
+    (4096, 8, 2, W.PADDED, 128, "normal"),      # 32 tiles of 256 ids
+    (1000, 8, 3, W.BINNED, 300, "ties"),        # K does not divide the tile: tokens straddle tiles
+    (777, 13, 5, W.PADDED, 8, "special"),
+    (3000, 64, 8, W.BINNED, 300, "normal"),
+    (20000, 8, 2, W.BINNED, 4000, "ties"),
+    (8192, 256, 8, W.PADDED, 128, "normal"),
+    (4096, 1024, 8, W.PADDED, 2, "normal"),      # expert x tile table too large: separate scan launch
+    (2000, 1, 1, W.BINNED, 2000, "normal"),
+]
+
+
+@pytest.mark.parametrize("T,E,K,layout,cm,kind", FUSED,
+                         ids=[f"T{c[0]}-E{c[1]}-K{c[2]}-{'bin' if c[3] == W.BINNED else 'pad'}" for c in FUSED])
+def test_route_prep_logits(T, E, K, layout, cm, kind):
+    """Gating fused with route_prep: gating outputs identical to
+    peg_router_topk's; routing arrays identical to the oracle's route_prep of
+    the oracle's gating (bit for bit); weights within the gating tolerance."""
+    print(f"[fused] T{T} E{E} K{K} layout{layout} {kind}", flush=True)
+    rng = np.random.default_rng(T + 7 * E + K)
+    lg = scores(rng, T, E, kind) if T > 0 else np.zeros((0, E), np.float32)
+    for gating in (peg.SOFTMAX, peg.SIGMOID):
+        lgd = to_dev(lg)
+        kw = dict(capacity=cm) if layout == W.BINNED else dict(pad_multiple=cm)
+        rg, top_g, w_g = peg.route_prep_logits(lgd, K, gating=gating, **kw)
+        top_s, w_s = peg.router_topk(lgd, K, gating=gating)
+        assert np.array_equal(to_host(top_g), to_host(top_s)), "fused experts != router_topk"
+        assert np.array_equal(to_host(w_g).view(np.uint32), to_host(w_s).view(np.uint32)), "fused weights"
+        top_o, w_o = oracle.router_topk(lg, W.F32, K, gating=gating)
+        assert np.array_equal(to_host(top_g), top_o)
+        check_weights(to_host(w_g), w_o, "fused weights vs oracle")
+        ro = oracle.route_prep(top_o, E, pad_multiple=cm if layout == W.PADDED else None)
+        assert np.array_equal(to_host(rg.indices), ro.indices)
+        assert np.array_equal(to_host(rg.bin_ids), ro.bin_ids)
+        assert np.array_equal(to_host(rg.tokens_per_expert), ro.tokens_per_expert)
+        assert np.array_equal(to_host(rg.bins), ro.bins)
+        if layout == W.PADDED:
+            assert np.array_equal(to_host(rg.padded_bins), ro.padded_bins)
+        cap = cm if layout == W.BINNED else None
+        assert np.array_equal(to_host(rg.slot_row), oracle.assignment_rows(ro, layout, cap))
