@@ -28,6 +28,20 @@ namespace peg {
 #define PEG_KBATCH 4
 #endif
 constexpr int kKBatch = PEG_KBATCH;  // expert rows loaded together before they are used
+#ifndef PEG_WGRAD_KBATCH
+#define PEG_WGRAD_KBATCH 2
+#endif
+constexpr int kWgradKBatch = PEG_WGRAD_KBATCH;  // the same for wgrad and the combine backward
+// Occupancy hint for wgrad / the combine backward (waves per SIMD the
+// register allocation must allow); 0 = the compiler's choice.
+#ifndef PEG_WGRAD_WAVES
+#define PEG_WGRAD_WAVES 0
+#endif
+#if PEG_WGRAD_WAVES > 0
+#define PEG_WGRAD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PEG_WGRAD_WAVES)))
+#else
+#define PEG_WGRAD_OCCUPANCY
+#endif
 
 __device__ __forceinline__ int64_t expert_rows(int64_t static_rows, const int32_t* padded_bins, int32_t E) {
     return padded_bins ? (int64_t)padded_bins[E - 1] : static_rows;
@@ -43,7 +57,7 @@ __device__ __forceinline__ int route_row(const int32_t* __restrict__ rows, int k
 
 // The columns of a token row are split into WPT contiguous slices, one per
 // wave; a wave covers its slice in passes of 64 lanes x U vectors.
-template <int DT, int VEC, int U, int WPT>
+template <int DT, int VEC, int U, int WPT, int KR>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restrict__ y, uint8_t* __restrict__ out,
                                                          int64_t nch, int64_t slice, int64_t T, int32_t K,
                                                          const int32_t* __restrict__ slot_row,
@@ -52,6 +66,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     using L = Lanes<DT, VEC>;
     using V = typename L::V;
     constexpr int N = L::N;
+    constexpr int KB = KR < kKBatch ? KR : kKBatch;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * TokenMap<WPT>::kTokensPerBlock + w / WPT;
     if (t >= T) return;  // no barrier in this kernel
@@ -61,10 +76,10 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     const int64_t R = expert_rows(static_rows, padded_bins, E);
     const int32_t* my_rows = slot_row + t * K;
     const float* my_w = weights ? weights + t * K : nullptr;
-    int r8[kRowsFast];
-    float w8[kRowsFast];
+    int r8[KR];
+    float w8[KR];
 #pragma unroll
-    for (int k = 0; k < kRowsFast; ++k) {
+    for (int k = 0; k < KR; ++k) {
         r8[k] = route_row(my_rows, k, K, R);
         w8[k] = (my_w && k < K) ? my_w[k] : 1.0f;
     }
@@ -78,10 +93,10 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
 #pragma unroll
             for (int i = 0; i < N; ++i) acc[u][i] = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < kRowsFast; kb += kKBatch) {
-            V v[kKBatch][U];
+        for (int kb = 0; kb < KR; kb += KB) {
+            V v[KB][U];
 #pragma unroll
-            for (int kk = 0; kk < kKBatch; ++kk) {
+            for (int kk = 0; kk < KB; ++kk) {
                 const int r = r8[kb + kk];
                 if (r < 0) continue;
                 const uint8_t* src = y + (int64_t)r * row_bytes;
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
                 }
             }
 #pragma unroll
-            for (int kk = 0; kk < kKBatch; ++kk) {
+            for (int kk = 0; kk < KB; ++kk) {
                 if (r8[kb + kk] < 0) continue;
                 const float wk = w8[kb + kk];
 #pragma unroll
@@ -106,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
                 }
             }
         }
-        for (int k = kRowsFast; k < K; ++k) {  // routes beyond the first 8, one at a time
+        for (int k = KR; k < K; ++k) {  // routes beyond the first 8, one at a time
             const int r = route_row(my_rows, k, K, R);
             if (r < 0) continue;
             const float wk = my_w ? my_w[k] : 1.0f;
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
 // in registers it is also stored into the gradient of the expert tensor, dy,
 // at every kept row of the token - scaled by that route's weight (DY == 2)
 // or as raw bits (DY == 1). Blocks past token_blocks zero dy's gap rows.
-template <int DT, int VEC, int U, int WPT, int DY>
+template <int DT, int VEC, int U, int WPT, int DY, int KR>
 __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
                                            float* __restrict__ wgrad, int64_t nch, int64_t slice, int64_t T,
                                            int32_t K, const int32_t* __restrict__ slot_row, int64_t static_rows,
@@ -151,6 +166,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
     using V = typename L::V;
     constexpr int N = L::N;
     constexpr int NW = kBlock / kWave;
+    constexpr int KB = KR < kWgradKBatch ? KR : kWgradKBatch;
     if constexpr (DY != 0) {
         if ((int64_t)blockIdx.x >= token_blocks) {
             zero_gap_rows<VEC>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins,
@@ -158,7 +174,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
             return;
         }
     }
-    __shared__ float red[NW][kRowsFast];
+    __shared__ float red[NW][KR];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int TPB = TokenMap<WPT>::kTokensPerBlock;
     const int64_t t = (int64_t)blockIdx.x * TPB + w / WPT;
@@ -171,19 +187,19 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
     const int64_t row_bytes = nch * VEC;
     const uint8_t* g_row = grad + (active ? t : 0) * row_bytes;
 
-    for (int k0 = 0; k0 < K; k0 += kRowsFast) {
-        int r8[kRowsFast];
-        float w8[kRowsFast];
+    for (int k0 = 0; k0 < K; k0 += KR) {
+        int r8[KR];
+        float w8[KR];
         bool any = false;
 #pragma unroll
-        for (int k = 0; k < kRowsFast; ++k) {
+        for (int k = 0; k < KR; ++k) {
             r8[k] = active ? route_row(my_rows, k0 + k, K, R) : -1;
             any |= r8[k] >= 0;
             if constexpr (DY == 2) w8[k] = r8[k] >= 0 ? weights[(active ? t : 0) * K + k0 + k] : 0.0f;
         }
-        float acc[kRowsFast];
+        float acc[KR];
 #pragma unroll
-        for (int k = 0; k < kRowsFast; ++k) acc[k] = 0.0f;
+        for (int k = 0; k < KR; ++k) acc[k] = 0.0f;
         if (any) {
             for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
                 V gv[U];
@@ -193,10 +209,10 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
                     if (c < c_end) gv[u] = stream_load<VEC>(g_row, c);
                 }
 #pragma unroll
-                for (int kb = 0; kb < kRowsFast; kb += kKBatch) {
-                    V v[kKBatch][U];
+                for (int kb = 0; kb < KR; kb += KB) {
+                    V v[KB][U];
 #pragma unroll
-                    for (int kk = 0; kk < kKBatch; ++kk) {
+                    for (int kk = 0; kk < KB; ++kk) {
                         const int r = r8[kb + kk];
                         if (r < 0) continue;
                         const uint8_t* src = y + (int64_t)r * row_bytes;
@@ -213,7 +229,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
                         float g[N];
                         L::unpack(gv[u], g);
 #pragma unroll
-                        for (int kk = 0; kk < kKBatch; ++kk) {
+                        for (int kk = 0; kk < KB; ++kk) {
                             const int r = r8[kb + kk];
                             if (r < 0) continue;
                             float f[N];
@@ -239,15 +255,15 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
             }
         }
 #pragma unroll
-        for (int k = 0; k < kRowsFast; ++k) {
+        for (int k = 0; k < KR; ++k) {
             if (r8[k] < 0) continue;
             const float s = wave_sum(acc[k]);
             if (lane == 0) red[w][k] = s;
         }
         lds_barrier();
-        if (threadIdx.x < TPB * kRowsFast) {
-            const int tl = threadIdx.x / kRowsFast;
-            const int k = threadIdx.x % kRowsFast;
+        if (threadIdx.x < TPB * KR) {
+            const int tl = threadIdx.x / KR;
+            const int k = threadIdx.x % KR;
             const int64_t tt = (int64_t)blockIdx.x * TPB + tl;
             if (tt < T && k0 + k < K) {
                 float s = 0.0f;
@@ -272,15 +288,16 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
 #define PEG_WGRAD_ARGS \
     y, grad, wgrad, nch, slice, T, K, slot_row, static_rows, padded_bins, E, weights, dy, dy_rows, layout, capacity, bins, token_blocks
 
-template <int DT, int VEC, int U, int WPT>
-__global__ __launch_bounds__(kBlock) void wgrad_kernel(PEG_WGRAD_PARAMS) {
-    wgrad_body<DT, VEC, U, WPT, 0>(PEG_WGRAD_ARGS);
+// KR: routes handled per pass over the row (2 when K <= 2, else 8).
+template <int DT, int VEC, int U, int WPT, int KR>
+__global__ __launch_bounds__(kBlock) PEG_WGRAD_OCCUPANCY void wgrad_kernel(PEG_WGRAD_PARAMS) {
+    wgrad_body<DT, VEC, U, WPT, 0, KR>(PEG_WGRAD_ARGS);
 }
 
 // DY: 1 = dy rows are dout rows as bits (no weights), 2 = weighted.
-template <int DT, int VEC, int U, int WPT, int DY>
-__global__ __launch_bounds__(kBlock) void combine_backward_kernel(PEG_WGRAD_PARAMS) {
-    wgrad_body<DT, VEC, U, WPT, DY>(PEG_WGRAD_ARGS);
+template <int DT, int VEC, int U, int WPT, int DY, int KR>
+__global__ __launch_bounds__(kBlock) PEG_WGRAD_OCCUPANCY void combine_backward_kernel(PEG_WGRAD_PARAMS) {
+    wgrad_body<DT, VEC, U, WPT, DY, KR>(PEG_WGRAD_ARGS);
 }
 #undef PEG_WGRAD_PARAMS
 #undef PEG_WGRAD_ARGS
@@ -314,12 +331,37 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
     return PEG_OK;
 }
 
+// Waves per token (WPT) and most vectors per lane per pass (UMAX) of the
+// combine and of wgrad / the combine backward, for K <= 2 (the _K2 values)
+// and for larger K; measured on the workloads.
 #ifndef PEG_COMBINE_UMAX
-#define PEG_COMBINE_UMAX 2  // most vectors per lane per pass in the combine
+#define PEG_COMBINE_UMAX 2
+#endif
+#ifndef PEG_COMBINE_WPT_K2
+#define PEG_COMBINE_WPT_K2 PEG_COMBINE_WPT
+#endif
+#ifndef PEG_COMBINE_UMAX_K2
+#define PEG_COMBINE_UMAX_K2 PEG_COMBINE_UMAX
 #endif
 #ifndef PEG_WGRAD_UMAX
-#define PEG_WGRAD_UMAX 2  // most vectors per lane per pass in wgrad
+#define PEG_WGRAD_UMAX 2
 #endif
+#ifndef PEG_WGRAD_WPT_K2
+#define PEG_WGRAD_WPT_K2 1
+#endif
+#ifndef PEG_WGRAD_UMAX_K2
+#define PEG_WGRAD_UMAX_K2 4
+#endif
+
+struct RowShape {
+    int wpt, umax;
+};
+static RowShape combine_shape(int32_t K) {
+    return K <= 2 ? RowShape{PEG_COMBINE_WPT_K2, PEG_COMBINE_UMAX_K2} : RowShape{PEG_COMBINE_WPT, PEG_COMBINE_UMAX};
+}
+static RowShape wgrad_shape(int32_t K) {
+    return K <= 2 ? RowShape{PEG_WGRAD_WPT_K2, PEG_WGRAD_UMAX_K2} : RowShape{PEG_WGRAD_WPT, PEG_WGRAD_UMAX};
+}
 
 // Vectors per lane per pass: 1, 2 or 4, capped.
 static int pass_vectors(int64_t slice, int cap) {
@@ -327,30 +369,33 @@ static int pass_vectors(int64_t slice, int cap) {
     return u < cap ? u : cap;
 }
 
+template <int DT, int VEC, int U>
+static peg_status combine_go(dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch, int64_t q,
+                             int64_t T, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
+#define PEG_COMBINE_LAUNCH(WPT, KR)                                                                            \
+    return launch(combine_kernel<DT, VEC, U, WPT, KR>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K, slot_row, \
+                  w, ra.static_rows, ra.padded_bins, E)
+    if (K <= 2) PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT_K2, 2);
+    PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT, kRowsFast);
+#undef PEG_COMBINE_LAUNCH
+}
+
 template <int DT, int VEC>
 static peg_status combine_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
                               int64_t q, int64_t T, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra,
                               int32_t E) {
-    if (u == 1)
-        return launch(combine_kernel<DT, VEC, 1, PEG_COMBINE_WPT>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K,
-                      slot_row, w, ra.static_rows, ra.padded_bins, E);
-    if (u == 2)
-        return launch(combine_kernel<DT, VEC, 2, PEG_COMBINE_WPT>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K,
-                      slot_row, w, ra.static_rows, ra.padded_bins, E);
-#if PEG_COMBINE_UMAX >= 4
-    return launch(combine_kernel<DT, VEC, 4, PEG_COMBINE_WPT>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K,
-                  slot_row, w, ra.static_rows, ra.padded_bins, E);
-#else
-    return PEG_ERR_LAUNCH;
-#endif
+    if (u == 1) return combine_go<DT, VEC, 1>(grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+    if (u == 2) return combine_go<DT, VEC, 2>(grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+    return combine_go<DT, VEC, 4>(grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
 }
 
 template <int DT>
 static peg_status combine_dispatch(int vec, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch, int64_t T,
                                    int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
-    const int64_t q = wave_slice(nch, PEG_COMBINE_WPT);
-    const int u = pass_vectors(q, PEG_COMBINE_UMAX);
-    const dim3 grid((unsigned)token_blocks(T, PEG_COMBINE_WPT));
+    const RowShape sh = combine_shape(K);
+    const int64_t q = wave_slice(nch, sh.wpt);
+    const int u = pass_vectors(q, sh.umax);
+    const dim3 grid((unsigned)token_blocks(T, sh.wpt));
     switch (vec) {
         case 16: return combine_vec<DT, 16>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
         case 8: return combine_vec<DT, 8>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
@@ -386,11 +431,12 @@ static peg_status wgrad_go(dim3 grid, hipStream_t s, const WgradArgs& a) {
     return launch(KERNEL, grid, dim3(kBlock), 0, s, a.y, a.g, a.wg, a.nch, a.slice, a.T, a.K, a.slot_row,        \
                   a.ra.static_rows, a.ra.padded_bins, a.E, a.weights, a.dy, a.dy_rows, a.layout, a.capacity, a.bins, \
                   a.token_blocks)
-    if constexpr (DY == 0) {
-        PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT>));
-    } else {
-        PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_WGRAD_WPT, DY>));
+    if (a.K <= 2) {
+        if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, 2>));
+        else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, DY, 2>));
     }
+    if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT, kRowsFast>));
+    else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_WGRAD_WPT, DY, kRowsFast>));
 #undef PEG_WGRAD_LAUNCH
 }
 
@@ -398,11 +444,7 @@ template <int DT, int VEC, int DY>
 static peg_status wgrad_u(int u, dim3 grid, hipStream_t s, const WgradArgs& a) {
     if (u == 1) return wgrad_go<DT, VEC, 1, DY>(grid, s, a);
     if (u == 2) return wgrad_go<DT, VEC, 2, DY>(grid, s, a);
-#if PEG_WGRAD_UMAX >= 4
     return wgrad_go<DT, VEC, 4, DY>(grid, s, a);
-#else
-    return PEG_ERR_LAUNCH;
-#endif
 }
 
 template <int DT, int DY>
@@ -466,9 +508,10 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const int64_t q = wave_slice(nch, PEG_WGRAD_WPT);
-    const int u = pass_vectors(q, PEG_WGRAD_UMAX);
-    const int64_t tb = token_blocks(T, PEG_WGRAD_WPT);
+    const RowShape sh = wgrad_shape(K);
+    const int64_t q = wave_slice(nch, sh.wpt);
+    const int u = pass_vectors(q, sh.umax);
+    const int64_t tb = token_blocks(T, sh.wpt);
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)grad, wgrad, nch, q, T, K, slot_row, ra, E, nullptr,
                       nullptr, 0, layout, capacity, bins, tb};
     return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
@@ -493,9 +536,10 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const int64_t q = wave_slice(nch, PEG_WGRAD_WPT);
-    const int u = pass_vectors(q, PEG_WGRAD_UMAX);
-    const int64_t tb = token_blocks(T, PEG_WGRAD_WPT);
+    const RowShape sh = wgrad_shape(K);
+    const int64_t q = wave_slice(nch, sh.wpt);
+    const int u = pass_vectors(q, sh.umax);
+    const int64_t tb = token_blocks(T, sh.wpt);
     const dim3 grid((unsigned)(tb + gap_blocks(dy_rows, nch)));
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)dout, wgrad, nch, q, T, K, slot_row, ra, E, weights,
                       (uint8_t*)dy, dy_rows, layout, capacity, bins, tb};
