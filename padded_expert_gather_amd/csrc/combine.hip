@@ -362,6 +362,21 @@ static RowShape combine_shape(int32_t K) {
 static RowShape wgrad_shape(int32_t K) {
     return K <= 2 ? RowShape{PEG_WGRAD_WPT_K2, PEG_WGRAD_UMAX_K2} : RowShape{PEG_WGRAD_WPT, PEG_WGRAD_UMAX};
 }
+#ifndef PEG_BACKWARD_WPT_K2
+#define PEG_BACKWARD_WPT_K2 PEG_WGRAD_WPT_K2
+#endif
+#ifndef PEG_BACKWARD_UMAX_K2
+#define PEG_BACKWARD_UMAX_K2 PEG_WGRAD_UMAX_K2
+#endif
+#ifndef PEG_BACKWARD_WPT
+#define PEG_BACKWARD_WPT PEG_WGRAD_WPT
+#endif
+#ifndef PEG_BACKWARD_UMAX
+#define PEG_BACKWARD_UMAX PEG_WGRAD_UMAX
+#endif
+static RowShape backward_shape(int32_t K) {
+    return K <= 2 ? RowShape{PEG_BACKWARD_WPT_K2, PEG_BACKWARD_UMAX_K2} : RowShape{PEG_BACKWARD_WPT, PEG_BACKWARD_UMAX};
+}
 
 // Vectors per lane per pass: 1, 2 or 4, capped.
 static int pass_vectors(int64_t slice, int cap) {
@@ -433,10 +448,10 @@ static peg_status wgrad_go(dim3 grid, hipStream_t s, const WgradArgs& a) {
                   a.token_blocks)
     if (a.K <= 2) {
         if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, 2>));
-        else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, DY, 2>));
+        else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT_K2, DY, 2>));
     }
     if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT, kRowsFast>));
-    else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_WGRAD_WPT, DY, kRowsFast>));
+    else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT, DY, kRowsFast>));
 #undef PEG_WGRAD_LAUNCH
 }
 
@@ -536,7 +551,7 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const RowShape sh = wgrad_shape(K);
+    const RowShape sh = backward_shape(K);
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
     const int64_t tb = token_blocks(T, sh.wpt);

@@ -81,9 +81,9 @@ inline int64_t token_blocks(int64_t T, int wpt) {
 // per-chunk count table of a tile (4 * ITEMS chunks of 64 x E ints) stays
 // within 32 KB of LDS.
 // Small inputs take fewer ids per thread (down to 1) until they make at least
-// kMinTiles tiles, so that more CUs share the work.
+// PEG_MIN_TILES tiles, so that more CUs share the work.
 #ifndef PEG_MIN_TILES
-#define PEG_MIN_TILES 32
+#define PEG_MIN_TILES 64
 #endif
 inline int prep_items(int32_t E) { return E <= 128 ? 16 : (E <= 256 ? 8 : (E <= 512 ? 4 : 2)); }
 inline int64_t tiles_of(int64_t total, int items) {
@@ -94,12 +94,23 @@ inline int tiled_items(int64_t total, int32_t E) {
     while (items > 1 && tiles_of(total, items) < PEG_MIN_TILES) items >>= 1;
     return items;
 }
+// Tiles of the gating fused with the histogram: about 128 tokens per tile
+// (one pass of a 1024-thread block at 8 lanes per token), so that the
+// gating is spread over many blocks.
+inline int fused_items(int64_t total, int32_t K, int32_t E) {
+    int items = 1;
+    while (items * 2 <= K / 2 && items * 2 <= prep_items(E)) items <<= 1;
+    return items < tiled_items(total, E) ? items : tiled_items(total, E);
+}
 inline int64_t prep_tiles(int64_t total, int32_t E) { return tiles_of(total, tiled_items(total, E)); }
 
 // Workspace: every call uses one region starting at offset 0.
 inline size_t ws_need(int64_t T, int32_t K, int32_t E) {
     int64_t total = T * (int64_t)K;
-    size_t tile_counts = (size_t)prep_tiles(total, E) * (size_t)E * 4;  // route_prep
+    int64_t ntiles = prep_tiles(total, E);
+    const int64_t nfused = K > 0 ? tiles_of(total, fused_items(total, K, E)) : 0;
+    if (nfused > ntiles) ntiles = nfused;
+    size_t tile_counts = (size_t)ntiles * (size_t)E * 4;  // route_prep (plain or fused with the gating)
     size_t slots = (size_t)total * 4;                                   // slot_row rebuild
     size_t bitmap = (size_t)((total + 31) / 32) * 4 + 64;               // validation
     size_t need = tile_counts;

@@ -19,7 +19,7 @@
 //   small: T*K < 8192 and its count table fits in LDS -> one 1024-thread
 //          block does everything (histogram, scans, placement) in one launch;
 //   tiled: tiles of 256*ITEMS ids (ITEMS shrinks for small inputs so that
-//          there are at least 32 tiles); a histogram launch, then a placement
+//          there are at least 64 tiles); a histogram launch, then a placement
 //          launch in which every block reads the (experts x tiles) count
 //          table and derives its own bases (block 0 also writes the bins);
 //          when that table is large, a single-block scan launch in between
@@ -90,11 +90,10 @@ __device__ __forceinline__ int position_row(int layout, int e, int capacity, int
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
-// Inputs of at least kBlock * PEG_MIN_TILES ids (32 tiles of 256) go to the
-// tiled path: two launches over 32+ CUs beat one CU from there on (measured
-// 7.7 vs 8.9 us at 8192 ids).
+// Inputs of 8192 ids and more go to the tiled path: two launches over 32+
+// CUs beat one CU from there on (measured 6.7 vs 8.9 us at 8192 ids).
 #ifndef PEG_SMALL_MAX_IDS
-#define PEG_SMALL_MAX_IDS (kBlock * PEG_MIN_TILES - 1)
+#define PEG_SMALL_MAX_IDS 8191
 #endif
 constexpr int64_t kSmallMaxIds = PEG_SMALL_MAX_IDS;
 constexpr size_t kSmallMaxTable = 48 * 1024;
@@ -340,19 +339,32 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
         }
         if (threadIdx.x == 0) s_n = bins[E - 1];
     } else {
-        // this tile's offset inside each expert, each expert's total, then
-        // scans over the experts for the starts
+        // each expert's total and this tile's offset inside it: the whole
+        // (experts x tiles) table is summed by all threads at once (coalesced
+        // reads, LDS atomics into pstart = totals and tbase = offsets), then
+        // scans over the experts give the starts
+        for (int e = threadIdx.x; e < E; e += kBlock) {
+            tbase[e] = 0;
+            pstart[e] = 0;
+        }
+        lds_barrier();
+        const int64_t table = ntiles * (int64_t)E;
+        for (int64_t i = threadIdx.x; i < table; i += kBlock) {
+            const int c = counts[i];
+            if (c != 0) {
+                const int e = (int)(i / ntiles);
+                atomicAdd(&pstart[e], c);
+                if (i - (int64_t)e * ntiles < (int64_t)blockIdx.x) atomicAdd(&tbase[e], c);
+            }
+        }
+        lds_barrier();
         int carry = 0, pcarry = 0;
         for (int e0 = 0; e0 < E; e0 += kBlock) {
             const int e = e0 + threadIdx.x;
             int before = 0, count = 0;
-            if (e < E) {
-                const int32_t* row = counts + (int64_t)e * ntiles;
-                for (int64_t t = 0; t < ntiles; ++t) {
-                    const int c = row[t];
-                    before += t < (int64_t)blockIdx.x ? c : 0;
-                    count += c;
-                }
+            if (e < E) {  // read before the scan's barriers; written back after them
+                count = pstart[e];
+                before = tbase[e];
             }
             int sum;
             const int pre = carry + block_exclusive_scan<kBlock>(count, scratch, &sum);

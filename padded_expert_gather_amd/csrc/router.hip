@@ -318,7 +318,7 @@ PEG_API peg_status peg_route_prep_logits(const void* logits, int32_t dtype, int6
     if (layout == PEG_PADDED && !padded_bins) return PEG_ERR_NULL_ARG;
     if (!ws || ws_bytes < ws_need(T, K, E)) return PEG_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int items = tiled_items(total, E);
+    const int items = fused_items(total, K, E);
     const int64_t ntiles = tiles_of(total, items);
     int32_t* counts = reinterpret_cast<int32_t*>(ws);
     if (ntiles > 0) {

@@ -72,6 +72,10 @@ CASES = [
     _case("tiled_items1_12k", 6000, 2, 8, 8, W.BF16, P, m=64, none_frac=0.05),
     _case("small_staged_6k", 3000, 2, 8, 8, W.BF16, P, m=64, none_frac=0.05),
     _case("tiled_8192", 4096, 2, 8, 8, W.BF16, P, m=128),
+    _case("tiled_E32", 5000, 4, 32, 8, W.BF16, B, cap=700, skew=0.05),
+    _case("tiled_E17_none", 9000, 2, 17, 8, W.BF16, P, m=16, none_frac=0.1),
+    _case("tiled_32768", 16384, 2, 8, 8, W.BF16, B, cap=5000, skew=0.3),
+    _case("tiled_32770", 16385, 2, 8, 8, W.BF16, P, m=64),
     _case("small_unstaged", 4000, 2, 64, 8, W.BF16, B, cap=100),
     _case("tile_2048", 1024, 2, 8, 16, W.BF16, B, cap=300),
     _case("tile_2049", 683, 3, 8, 16, W.BF16, P, m=8),
