@@ -340,21 +340,36 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
         if (threadIdx.x == 0) s_n = bins[E - 1];
     } else {
         // each expert's total and this tile's offset inside it: the whole
-        // (experts x tiles) table is summed by all threads at once (coalesced
-        // reads, LDS atomics into pstart = totals and tbase = offsets), then
-        // scans over the experts give the starts
+        // (experts x tiles) table (expert-major) is summed by all threads at
+        // once, each over its own contiguous segment, in registers, with one
+        // LDS atomic per expert the segment touches (pstart = totals, tbase =
+        // offsets); then scans over the experts give the starts
         for (int e = threadIdx.x; e < E; e += kBlock) {
             tbase[e] = 0;
             pstart[e] = 0;
         }
         lds_barrier();
-        const int64_t table = ntiles * (int64_t)E;
-        for (int64_t i = threadIdx.x; i < table; i += kBlock) {
-            const int c = counts[i];
-            if (c != 0) {
-                const int e = (int)(i / ntiles);
-                atomicAdd(&pstart[e], c);
-                if (i - (int64_t)e * ntiles < (int64_t)blockIdx.x) atomicAdd(&tbase[e], c);
+        {
+            const int64_t table = ntiles * (int64_t)E;
+            const int64_t seg = (table + kBlock - 1) / kBlock;
+            const int64_t i0 = (int64_t)threadIdx.x * seg;
+            const int64_t i1 = i0 + seg < table ? i0 + seg : table;
+            if (i0 < i1) {
+                int e = (int)(i0 / ntiles);
+                int64_t t = i0 - (int64_t)e * ntiles;
+                int run = 0, run_before = 0;
+                for (int64_t i = i0; i < i1; ++i) {
+                    const int c = counts[i];
+                    run += c;
+                    run_before += t < (int64_t)blockIdx.x ? c : 0;
+                    if (++t == ntiles || i + 1 == i1) {  // end of this expert's row, or of the segment
+                        if (run) atomicAdd(&pstart[e], run);
+                        if (run_before) atomicAdd(&tbase[e], run_before);
+                        run = run_before = 0;
+                        t = 0;
+                        ++e;
+                    }
+                }
             }
         }
         lds_barrier();
