@@ -4,7 +4,8 @@ One step = one pass of the whole path over one routed batch: (routing-map
 compaction, for the compaction workload) -> route_prep -> gather (binned or
 padded) -> weighted scatter-combine -> wgrad, with every buffer preallocated
 and every call going through the C ABI of libpeg.so on torch's current
-stream. Steps rotate over several copies of the input (distinct buffers) so
+stream. With --from-logits a step starts from the router scores instead:
+gating fused with route_prep replaces route_prep. Steps rotate over several copies of the input (distinct buffers) so
 that the bytes of a step are not served from the 256 MB Infinity Cache left
 warm by the previous step.
 
@@ -80,6 +81,9 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
     ap.add_argument("--no-router", action="store_true", help="skip timing the router gating")
+    ap.add_argument("--from-logits", action="store_true",
+                    help="start each step from the router scores: gating fused with route_prep replaces route_prep "
+                         "(workloads with router scores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device-to-device copies (reference for the HBM byte counters) and exit")
     return ap.parse_args()
@@ -172,10 +176,20 @@ class Step:
         if wl.routing_map is not None:
             self.calls["compact"] = (lib.peg_routing_map_compact,
                                      (P(self.probs), 0, P(self.rmap), T, E, wl.topk, P(self.w), P(self.top), st))
-        self.calls["route_prep"] = (lib.peg_route_prep,
-                                    (P(self.top), T, K, E, wl.layout, cap, m, P(self.indices), P(self.bin_ids),
-                                     P(self.tpe), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.ws),
-                                     wsb, st))
+        if host.get("from_logits"):
+            # gating of the router scores fused with route_prep, into the
+            # step's own routing and weight buffers
+            self.logits_step = host["logits"].to(dev)
+            self.calls["route_prep_logits"] = (
+                lib.peg_route_prep_logits,
+                (P(self.logits_step), 0, T, E, K, 0, 1, wl.layout, cap, m, P(self.top), P(self.w), P(self.indices),
+                 P(self.bin_ids), P(self.tpe), P(self.bins), P(self.padded_bins), P(self.slot_row), P(self.ws), wsb,
+                 st))
+        else:
+            self.calls["route_prep"] = (lib.peg_route_prep,
+                                        (P(self.top), T, K, E, wl.layout, cap, m, P(self.indices), P(self.bin_ids),
+                                         P(self.tpe), P(self.bins), P(self.padded_bins), P(self.slot_row),
+                                         P(self.ws), wsb, st))
         if wl.layout == W.BINNED:
             self.calls["gather"] = (lib.peg_gather_binned,
                                     (P(self.x), wl.dtype, T, H, K, E, cap, P(self.indices), P(self.bin_ids),
@@ -360,6 +374,10 @@ def main():
     bytes_step = sum(ab.values())
     host["no_backward"] = args.no_backward
     host["no_router"] = args.no_router
+    if args.from_logits and wl.logits is None:
+        print(f"--from-logits: workload {wl.name} has no router scores", file=sys.stderr)
+        sys.exit(2)
+    host["from_logits"] = args.from_logits
     per_set = (wl.T * wl.H * s) * 3 + sz["R"] * wl.H * s * (1 if args.no_backward else 2)
     sets = args.sets or max(2, min(16, math.ceil(2 * 2 ** 30 / per_set)))
     log(f"R={sz['R']} N={sz['N']} U={sz['U']} step bytes={bytes_step / 1e6:.1f} MB, {sets} input copies")
@@ -449,7 +467,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K,
                    "layout": "binned" if wl.layout == W.BINNED else "padded",
                    "capacity": wl.capacity or None, "pad_multiple": wl.pad_multiple or None,
-                   "compaction": wl.routing_map is not None, "input_copies": sets,
+                   "compaction": wl.routing_map is not None, "input_copies": sets, "from_logits": args.from_logits,
                    "rows": sz["R"], "kept": sz["N"], "tokens_with_route": sz["U"]},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "routed_tokens_per_s": round(wl.T / (ms_step / 1e3), 1),

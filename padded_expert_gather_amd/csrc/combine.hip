@@ -335,7 +335,7 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
 // combine and of wgrad / the combine backward, for K <= 2 (the _K2 values)
 // and for larger K; measured on the workloads.
 #ifndef PEG_COMBINE_UMAX
-#define PEG_COMBINE_UMAX 2
+#define PEG_COMBINE_UMAX 4
 #endif
 #ifndef PEG_COMBINE_WPT_K2
 #define PEG_COMBINE_WPT_K2 PEG_COMBINE_WPT

@@ -15,9 +15,15 @@ namespace peg {
 #define PEG_GAP_UNITS 8192  // target vectors zeroed per gap block
 #endif
 #ifndef PEG_GAP_MAX
-#define PEG_GAP_MAX 2048  // most gap blocks per launch
+#define PEG_GAP_MAX 8192  // most gap blocks per launch
 #endif
-constexpr int kZeroUnroll = 4;
+#ifndef PEG_ZERO_UNROLL
+#define PEG_ZERO_UNROLL 4  // zero stores in flight per thread
+#endif
+#ifndef PEG_NT_STORE_ZERO
+#define PEG_NT_STORE_ZERO PEG_NT_STORE  // the nontemporal hint on the zero stores
+#endif
+constexpr int kZeroUnroll = PEG_ZERO_UNROLL;
 
 // Gap blocks for a tensor of up to max_gap_rows gap rows of nch vectors.
 inline int64_t gap_blocks(int64_t max_gap_rows, int64_t nch) {
@@ -98,7 +104,7 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
 #pragma unroll
             for (int j = 0; j < kZeroUnroll; ++j) {
                 const int64_t uu = u + (int64_t)j * kBlock;
-                if (uu < seg_end) stream_store<VEC>(out, shift + uu, z);
+                if (uu < seg_end) stream_store<VEC, PEG_NT_STORE_ZERO>(out, shift + uu, z);
             }
         }
         u0 = seg_end > u0 ? seg_end : u0;
