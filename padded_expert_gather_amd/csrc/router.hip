@@ -14,55 +14,58 @@
 //
 // Design: a group of G lanes (8, or 16/32 when E > 256) owns one token, so
 // a wave serves 64/G tokens; lane g holds the scores of experts g, g + G,
-// g + 2G, ... (CPL <= 32 of them). Each score becomes a 64-bit key,
-// (order-preserving image of the float) << 32 | (~expert id), so that one
-// unsigned maximum picks the highest score and, on ties, the lowest id. K
-// rounds of [lane maximum over its keys, maximum over the group, the owner
-// retires the winner] give the K experts in rank order, exactly (no float
-// arithmetic decides the selection). Group reductions use DPP lane moves
-// (quad permutes, half-row and row mirrors), which are plain VALU
-// operations; only groups wider than a 16-lane row also cross rows through
-// the LDS crossbar. Result k is kept by lane k % G, so the K outputs of a
-// token are written by the group's lanes side by side.
+// g + 2G, ... (CPL <= 32 of them) as order-preserving 32-bit keys. K rounds
+// of [group maximum of the keys, group minimum of the ids holding it, the
+// owner clears the winner] give the K experts in rank order, exactly (no
+// float arithmetic decides the selection). Group reductions use DPP lane
+// moves (quad permutes, half-row and row mirrors), plain VALU operations;
+// only groups wider than a 16-lane row also cross rows through the LDS
+// crossbar. Result k is kept by lane k % G, so the K outputs of a token are
+// written by the group's lanes side by side, and the weights of all K are
+// evaluated after the rounds, by all lanes at once.
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
 namespace peg {
 
 // Order-preserving image of a float's value as an unsigned integer: larger
-// values give larger images; NaN gives 0, below every number; -0 maps as +0.
+// values give larger images (every number maps to 0x007FFFFF or more); NaN
+// gives 1, below every number; -0 maps as +0; 0 is left free to mark an
+// expert that is absent or already chosen.
 __device__ __forceinline__ uint32_t score_key(float f) {
-    if (f != f) return 0u;
+    if (f != f) return 1u;
     uint32_t b = __float_as_uint(f);
     if ((b & 0x7FFFFFFFu) == 0u) b = 0u;  // -0 -> +0
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Inverse of score_key for every key a number gives (0 decodes to NaN).
+// Inverse of score_key for every key a number gives (1 decodes to NaN).
 __device__ __forceinline__ float key_score(uint32_t k) {
-    if (k == 0u) return __uint_as_float(0x7FC00000u);
+    if (k <= 1u) return __uint_as_float(0x7FC00000u);
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t max_step(uint64_t v) {
-    const uint64_t o = ((uint64_t)(uint32_t)dpp_read<CTRL>((int)(v >> 32)) << 32) |
-                       (uint32_t)dpp_read<CTRL>((int)(uint32_t)v);
-    return o > v ? o : v;
+// Maximum / minimum over the G lanes of a group, every lane of it gets the
+// result (DPP lane moves inside 16-lane rows, the LDS crossbar beyond).
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+    v = max(v, (uint32_t)dpp_read<kDppQuadXor1>((int)v));
+    v = max(v, (uint32_t)dpp_read<kDppQuadXor2>((int)v));
+    v = max(v, (uint32_t)dpp_read<kDppHalfMirror>((int)v));
+    if constexpr (G >= 16) v = max(v, (uint32_t)dpp_read<kDppRowMirror>((int)v));
+#pragma unroll
+    for (int d = 16; d < G; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, G));
+    return v;
 }
 
-// Maximum over the G lanes of a group; every lane of it gets the result.
 template <int G>
-__device__ __forceinline__ uint64_t group_max(uint64_t v) {
-    v = max_step<kDppQuadXor1>(v);
-    v = max_step<kDppQuadXor2>(v);
-    v = max_step<kDppHalfMirror>(v);
-    if constexpr (G >= 16) v = max_step<kDppRowMirror>(v);
+__device__ __forceinline__ uint32_t group_min(uint32_t v) {
+    v = min(v, (uint32_t)dpp_read<kDppQuadXor1>((int)v));
+    v = min(v, (uint32_t)dpp_read<kDppQuadXor2>((int)v));
+    v = min(v, (uint32_t)dpp_read<kDppHalfMirror>((int)v));
+    if constexpr (G >= 16) v = min(v, (uint32_t)dpp_read<kDppRowMirror>((int)v));
 #pragma unroll
-    for (int d = 16; d < G; d <<= 1) {
-        const uint64_t o = __shfl_xor(v, d, G);
-        v = o > v ? o : v;
-    }
+    for (int d = 16; d < G; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d, G));
     return v;
 }
 
@@ -87,83 +90,106 @@ __device__ __forceinline__ float load_score(const void* p, int64_t i) {
 }
 
 // Gating of token t by the G lanes of a group (lane g): on return, lane g
-// holds the results k = j * G + g (k < K) in sel_e[j] (expert) and sel_w[j]
-// (weight). Every lane of the group must call it.
-template <int DT, int G, int CPL>
+// holds the results k = j * G + g (k < K, j < KS) in sel_e[j] (expert) and
+// sel_w[j] (weight). KS = 1 when K <= G. Every lane of the group must call it.
+//
+// A round picks the highest score key over the group (a 32-bit maximum),
+// then the lowest expert id holding it (a 32-bit minimum over the lanes whose
+// key ties); the winner's key is cleared. The scores of the chosen experts
+// are kept and turned into weights after the K rounds, all lanes at once.
+// exp is the hardware base-2 exponential of x * log2(e) (__expf): its
+// relative error grows with |x| as about |x| * 2^-24, well inside the 1e-5
+// tolerance for the score gaps that carry weight.
+template <int DT, int G, int CPL, int KS>
 __device__ __forceinline__ void gate_token(const void* __restrict__ logits, int64_t t, int32_t E, int32_t K,
-                                           int32_t gating, int32_t normalize, int g, int32_t (&sel_e)[CPL],
-                                           float (&sel_w)[CPL]) {
+                                           int32_t gating, int32_t normalize, int g, int32_t (&sel_e)[KS],
+                                           float (&sel_w)[KS]) {
     static_assert(G >= 8 && G <= kWave && (G & (G - 1)) == 0, "group of 8..64 lanes");
-    uint64_t key[CPL];
+    uint32_t key[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = g + j * G;
-        key[j] = e < E ? ((uint64_t)score_key(load_score<DT>(logits, t * E + e)) << 32) |
-                             (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
-                       : 0ull;
+        key[j] = e < E ? score_key(load_score<DT>(logits, t * E + e)) : 0u;
     }
-    uint64_t top = 0;
+    uint32_t top = 0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) top = key[j] > top ? key[j] : top;
+    for (int j = 0; j < CPL; ++j) top = max(top, key[j]);
     top = group_max<G>(top);
-    const float m = key_score((uint32_t)(top >> 32));  // the highest score (NaN if every score is)
+    const float m = key_score(top);  // the highest score (NaN if every score is)
     // softmax denominator over all E scores
     float denom = 1.0f;
     if (gating == 0) {
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
-            if (g + j * G < E) s += expf(key_score((uint32_t)(key[j] >> 32)) - m);
+            if (g + j * G < E) s += __expf(key_score(key[j]) - m);
         denom = group_sum<G>(s);
+    }
+    float sel_l[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        sel_e[j] = 0;
+        sel_l[j] = 0.0f;
+    }
+    for (int k = 0; k < K; ++k) {
+        uint32_t best = 0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) best = max(best, key[j]);
+        best = group_max<G>(best);
+        // lowest id among the group's keys equal to best: within a lane the
+        // ids rise with j, so its first such slot
+        uint32_t id = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = CPL - 1; j >= 0; --j)
+            if (key[j] == best) id = (uint32_t)(g + j * G);
+        const int32_t e = (int32_t)group_min<G>(id);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            if (g + j * G == e) key[j] = 0u;
+        if constexpr (KS == 1) {
+            if (k == g) {
+                sel_e[0] = e;
+                sel_l[0] = key_score(best);
+            }
+        } else {
+            if (k % G == g) {
+#pragma unroll
+                for (int j = 0; j < KS; ++j)
+                    if (j == k / G) {
+                        sel_e[j] = e;
+                        sel_l[j] = key_score(best);
+                    }
+            }
+        }
     }
     // Renormalised sigmoid with a negative top score m: every chosen sigmoid
     // carries the factor exp(m), which cancels in the ratio; it is taken out
     // (q = exp(l - m) / (1 + exp(l)) instead of 1 / (1 + exp(-l))) so that
     // exp(-l) cannot overflow fp32 and turn the weights into 0 / 0.
     const bool shifted = gating != 0 && normalize && m < 0.0f;
-    // K selection rounds; result k lands in slot k / G of lane k % G.
+    float sel_sum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        sel_e[j] = 0;
-        sel_w[j] = 0.0f;
-    }
-    for (int k = 0; k < K; ++k) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) best = key[j] > best ? key[j] : best;
-        best = group_max<G>(best);
-        const int32_t e = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
-        if (e % G == g) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j)
-                if (j == e / G) key[j] = 0;
+    for (int j = 0; j < KS; ++j) {
+        float p = 0.0f;
+        if (j * G + g < K) {
+            const float l = sel_l[j];
+            if (gating == 0) p = __expf(l - m) / denom;
+            else if (shifted) p = __expf(l - m) / (1.0f + __expf(l));
+            else p = 1.0f / (1.0f + __expf(-l));
         }
-        if (k % G == g) {
-            const float l = key_score((uint32_t)(best >> 32));
-            float p;
-            if (gating == 0) p = expf(l - m) / denom;
-            else if (shifted) p = expf(l - m) / (1.0f + expf(l));
-            else p = 1.0f / (1.0f + expf(-l));
-#pragma unroll
-            for (int j = 0; j < CPL; ++j)
-                if (j == k / G) {
-                    sel_e[j] = e;
-                    sel_w[j] = p;
-                }
-        }
+        sel_w[j] = p;
+        sel_sum += p;
     }
     if (normalize) {
-        float sel_sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) sel_sum += sel_w[j];  // slots past K hold 0
         sel_sum = group_sum<G>(sel_sum);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) sel_w[j] = sel_w[j] / sel_sum;
+        for (int j = 0; j < KS; ++j) sel_w[j] = sel_w[j] / sel_sum;
     }
 }
 
-// G lanes per token, CPL scores per lane (E <= G * CPL).
-template <int DT, int G, int CPL>
+// G lanes per token, CPL scores per lane (E <= G * CPL), KS result slots per
+// lane (K <= G * KS).
+template <int DT, int G, int CPL, int KS>
 __global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restrict__ logits, int64_t T, int32_t E,
                                                              int32_t K, int32_t gating, int32_t normalize,
                                                              int32_t* __restrict__ top_experts,
@@ -172,11 +198,11 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restr
     const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
     if (t >= T) return;  // whole groups leave together: reductions stay within live groups
     const int g = threadIdx.x % G;
-    int32_t sel_e[CPL];
-    float sel_w[CPL];
-    gate_token<DT, G, CPL>(logits, t, E, K, gating, normalize, g, sel_e, sel_w);
+    int32_t sel_e[KS];
+    float sel_w[KS];
+    gate_token<DT, G, CPL, KS>(logits, t, E, K, gating, normalize, g, sel_e, sel_w);
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
+    for (int j = 0; j < KS; ++j) {
         const int k = j * G + g;
         if (k < K) {
             top_experts[t * K + k] = sel_e[j];
@@ -193,7 +219,7 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restr
 // table the placement pass reads.
 constexpr int kHistThreads = 1024;  // gating lanes of a tile: 128 tokens per pass at 8 lanes per token
 
-template <int DT, int G, int CPL>
+template <int DT, int G, int CPL, int KS>
 __global__ __launch_bounds__(kHistThreads) void router_hist_kernel(const void* __restrict__ logits, int64_t T, int32_t E,
                                                              int32_t K, int32_t gating, int32_t normalize,
                                                              int64_t tile, int64_t ntiles,
@@ -213,12 +239,12 @@ __global__ __launch_bounds__(kHistThreads) void router_hist_kernel(const void* _
     for (int64_t t0 = t_first; t0 <= t_last; t0 += TPB) {
         const int64_t t = t0 + threadIdx.x / G;
         if (t > t_last) continue;  // whole groups skip together
-        int32_t sel_e[CPL];
-        float sel_w[CPL];
-        gate_token<DT, G, CPL>(logits, t, E, K, gating, normalize, g, sel_e, sel_w);
+        int32_t sel_e[KS];
+        float sel_w[KS];
+        gate_token<DT, G, CPL, KS>(logits, t, E, K, gating, normalize, g, sel_e, sel_w);
         const bool owner = t * K >= lo;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
+        for (int j = 0; j < KS; ++j) {
             const int k = j * G + g;
             if (k < K) {
                 const int64_t a = t * K + k;
@@ -245,15 +271,21 @@ struct GateArgs {
     int32_t* counts;
 };
 
-template <int DT, int G, int CPL>
-static peg_status gate_go(hipStream_t s, const GateArgs& a) {
+template <int DT, int G, int CPL, int KS>
+static peg_status gate_launch(hipStream_t s, const GateArgs& a) {
     if (a.ntiles > 0)
-        return launch(router_hist_kernel<DT, G, CPL>, dim3((unsigned)a.ntiles), dim3(kHistThreads), 0, s, a.logits, a.T,
-                      a.E, a.K, a.gating, a.normalize, a.tile, a.ntiles, a.top, a.w, a.counts);
+        return launch(router_hist_kernel<DT, G, CPL, KS>, dim3((unsigned)a.ntiles), dim3(kHistThreads), 0, s,
+                      a.logits, a.T, a.E, a.K, a.gating, a.normalize, a.tile, a.ntiles, a.top, a.w, a.counts);
     constexpr int TPB = kBlock / G;
     const dim3 grid((unsigned)((a.T + TPB - 1) / TPB));
-    return launch(router_topk_kernel<DT, G, CPL>, grid, dim3(kBlock), 0, s, a.logits, a.T, a.E, a.K, a.gating,
+    return launch(router_topk_kernel<DT, G, CPL, KS>, grid, dim3(kBlock), 0, s, a.logits, a.T, a.E, a.K, a.gating,
                   a.normalize, a.top, a.w);
+}
+
+template <int DT, int G, int CPL>
+static peg_status gate_go(hipStream_t s, const GateArgs& a) {
+    if (a.K <= G) return gate_launch<DT, G, CPL, 1>(s, a);
+    return gate_launch<DT, G, CPL, CPL>(s, a);
 }
 
 template <int DT>

@@ -7,10 +7,11 @@ bound is
 i.e. the fp32 relative tolerance used for every fp32 output here, plus an
 absolute floor below which fp32 exp underflows (a probability under 1e-30
 is zero to both). The fp32 evaluation error it has to cover: the rounding of
-(score - max) scaled by its size (|score - max| * 2^-24 relative), one or two
-ulps of exp, a sum of up to 1024 terms in a tree of depth <= 22, and two
-divisions: under 4e-6 for score gaps below 50. NaN must appear at the same
-places on both sides (rows whose formulas give NaN).
+(score - max) scaled by its size (|score - max| * 2^-24 relative), the
+hardware exponential's error (about (|x| * log2(e) + 1) * 2^-23 relative), a
+sum of up to 1024 terms in a tree of depth <= 22, and two divisions: under
+6e-6 for score gaps below 40. NaN must appear at the same places on both
+sides (rows whose formulas give NaN).
 """
 import math
 
