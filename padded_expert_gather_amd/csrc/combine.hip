@@ -167,17 +167,20 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
     constexpr int N = L::N;
     constexpr int NW = kBlock / kWave;
     constexpr int KB = KR < kWgradKBatch ? KR : kWgradKBatch;
+    int64_t tblock = blockIdx.x;  // token-block index
     if constexpr (DY != 0) {
-        if ((int64_t)blockIdx.x >= token_blocks) {
-            zero_gap_rows<VEC>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins,
-                               (int64_t)blockIdx.x - token_blocks, (int64_t)gridDim.x - token_blocks);
+        const int64_t nz = (int64_t)gridDim.x - token_blocks;
+        int64_t role_index;
+        if (gap_role(blockIdx.x, gridDim.x, nz, &role_index)) {
+            zero_gap_rows<VEC>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins, role_index, nz);
             return;
         }
+        tblock = role_index;
     }
     __shared__ float red[NW][KR];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int TPB = TokenMap<WPT>::kTokensPerBlock;
-    const int64_t t = (int64_t)blockIdx.x * TPB + w / WPT;
+    const int64_t t = tblock * TPB + w / WPT;
     const bool active = t < T;  // every wave still takes part in the barriers
     const int lane = lane_id();
     const int64_t c_begin = (w % WPT) * slice;
@@ -264,7 +267,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
         if (threadIdx.x < TPB * KR) {
             const int tl = threadIdx.x / KR;
             const int k = threadIdx.x % KR;
-            const int64_t tt = (int64_t)blockIdx.x * TPB + tl;
+            const int64_t tt = tblock * TPB + tl;
             if (tt < T && k0 + k < K) {
                 float s = 0.0f;
                 if (route_row(slot_row + tt * K, k0 + k, K, R) >= 0) {

@@ -35,11 +35,13 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     using V = typename VecOf<VEC>::T;
     const int64_t row_bytes = nch * VEC;
 
-    if ((int64_t)blockIdx.x < token_blocks) {
+    int64_t role_index;
+    const int64_t nz = (int64_t)gridDim.x - token_blocks;
+    if (!gap_role(blockIdx.x, gridDim.x, nz, &role_index)) {
         // ---------------- token row -> its expert rows ----------------
         // (no barrier in this part: waves run independently)
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-        const int64_t t = (int64_t)blockIdx.x * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+        const int64_t t = role_index * TokenMap<WPT>::kTokensPerBlock + w / WPT;
         if (t >= T) return;
         const int lane = lane_id();
         const int64_t c_begin = (w % WPT) * slice;
@@ -96,8 +98,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     }
 
     // ---------------- zero the gap rows ----------------
-    zero_gap_rows<VEC>(out, nch, out_rows, layout, E, capacity, bins, padded_bins,
-                       (int64_t)blockIdx.x - token_blocks, (int64_t)gridDim.x - token_blocks);
+    zero_gap_rows<VEC>(out, nch, out_rows, layout, E, capacity, bins, padded_bins, role_index, nz);
 }
 
 struct GatherArgs {
