@@ -80,6 +80,10 @@ CASES = [
     _case("tile_2048", 1024, 2, 8, 16, W.BF16, B, cap=300),
     _case("tile_2049", 683, 3, 8, 16, W.BF16, P, m=8),
     _case("tile_2047", 2047, 1, 8, 16, W.BF16, B, cap=300),
+    _case("K12_binned", 300, 12, 16, 72, W.BF16, B, cap=150, skew=0.1),
+    _case("K16_padded_f32", 200, 16, 32, 40, W.F32, P, m=8, none_frac=0.2),
+    _case("K9_f16", 150, 9, 12, 24, W.F16, B, cap=90),
+    _case("H16384_bf16", 64, 2, 4, 16384, W.BF16, P, m=16),
     _case("T0_binned", 0, 2, 4, 32, W.BF16, B, cap=4),
     _case("T0_padded", 0, 2, 4, 32, W.BF16, P, m=4),
 ]
