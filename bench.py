@@ -101,6 +101,35 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
 
 
+def copy_ceiling(torch, hip, stream):
+    """Device-to-device copy rate of this GPU (torch's copy of 1 GiB between
+    two buffers, read + write bytes per second), timed with HIP events: the
+    achievable ceiling that a kernel moving as many bytes as it reads can
+    reach."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(5):
+        a, b = hip.create(), hip.create()
+        hip.record(a, stream)
+        dst.copy_(src)
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        ms.append(hip.elapsed_ms(a, b))
+    ms.sort()
+    del src, dst
+    return round(2 * n / (ms[len(ms) // 2] / 1e3) / 1e9, 1)
+
+
+def median(xs):
+    ys = sorted(xs)
+    return ys[len(ys) // 2]
+
+
 class HipEvents:
     """HIP events from the process's HIP runtime (the one torch loaded),
     created without the system-scope fence so that recording one between two
@@ -415,7 +444,8 @@ def main():
         for n in names:
             ms = [hip.elapsed_ms(evs[i][n][0], evs[i][n][1]) for i in range(args.steps)]
             avg = sum(ms) / len(ms)
-            entry = {"avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2)}
+            entry = {"avg_us": round(avg * 1e3, 2), "median_us": round(median(ms) * 1e3, 2),
+                     "min_us": round(min(ms) * 1e3, 2)}
             if n in ab:
                 entry["bytes"] = ab[n]
                 entry["GBps"] = round(ab[n] / (avg / 1e3) / 1e9, 1)
@@ -446,13 +476,17 @@ def main():
         ms = [hip.elapsed_ms(a, b) for a, b in bevs]
         avg = sum(ms) / len(ms)
         bb = extra_bytes[name]
-        extras[name] = {"avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2), "bytes": bb,
+        extras[name] = {"avg_us": round(avg * 1e3, 2), "median_us": round(median(ms) * 1e3, 2),
+                        "min_us": round(min(ms) * 1e3, 2), "bytes": bb,
                         "GBps": round(bb / (avg / 1e3) / 1e9, 1),
                         "frac_peak": round(bb / (avg / 1e3) / 1e9 / PEAK_GBS, 4)}
         if name == "combine_backward":
             extras[name]["traffic"] = traffic_for("backward", wl.name)
         if name in ("router_topk", "route_prep_logits"):
             extras[name]["tokens_per_s"] = round(wl.T / (avg / 1e3), 1)
+    copy_GBps = copy_ceiling(torch, HipEvents(), steps_obj[0].stream) if not args.no_events else None
+    if roofline and copy_GBps:
+        roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / copy_GBps, 4)
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -475,6 +509,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "copy_ceiling_GBps": copy_GBps,
         "outside_step": extras,
         "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},
     }

@@ -446,7 +446,10 @@ static int id_bits(int E) {
 
 // Tiles whose histogram table (experts x tiles) is at most this many ints
 // skip the separate scan launch: each placement block reads the table.
-constexpr int64_t kMergedMaxTable = 16384;
+#ifndef PEG_MERGED_MAX_TABLE
+#define PEG_MERGED_MAX_TABLE 16384
+#endif
+constexpr int64_t kMergedMaxTable = PEG_MERGED_MAX_TABLE;
 
 template <int ITEMS>
 static peg_status place_tiles(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
