@@ -10,14 +10,17 @@
 //   wgrad: wgrad[a] = <y[row(a)], grad[a / K]> for kept a, else 0 (Workflow
 //     step 6 of both pages; fp32 accumulation per their Ascend Guardrails).
 //
+//   combine backward: dy[row(a)] = w[a] * dout[a / K] in the expert layout
+//     (zero gap rows) and wgrad of dout, in one pass over dout.
+//
 // How: token-major. The token's rows (and weights) come in by wave-uniform
 // scalar loads, and each of the token's waves streams its slice of the H
-// columns in 16-byte lanes: every kept expert row is read
-// once, the output row (combine) is written once, the gradient row (wgrad)
-// is read once for all K dots. Accumulation is fp32 FMA; the wgrad dots
-// finish with a wave64 butterfly and a sum over the token's waves in LDS.
-// Rows that are
-// unused capacity, padding or dropped are never read.
+// columns in 16-byte lanes: every kept expert row is read once, the output
+// row (combine) is written once, the gradient row (wgrad) is read once for
+// all K dots. Accumulation is fp32 FMA; the wgrad dots finish with a DPP wave
+// reduction and a sum over the token's waves in LDS. The kernels are compiled
+// for 2 routes per pass (K <= 2: fewer registers, full occupancy) and for 8.
+// Rows that are unused capacity, padding or dropped are never read.
 #include "gaps.hpp"
 #include "peg_device.hpp"
 #include "peg_host.hpp"

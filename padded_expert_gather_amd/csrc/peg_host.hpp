@@ -38,7 +38,8 @@ inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, con
 // The token kernels give each token WPT waves (4, 2 or 1) of a 4-wave
 // block, so a block holds 4 / WPT tokens. Measured on MI355X: the gather
 // likes 2 waves per token for rows of at most 512 vectors and 4 above, the
-// combine 4, the wgrad 2.
+// combine 4, wgrad and the combine backward 2 (1 when K <= 2; the per-K
+// values sit with those kernels).
 #ifndef PEG_COMBINE_WPT
 #define PEG_COMBINE_WPT 4
 #endif
