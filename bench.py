@@ -379,7 +379,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the data path is a "
-              f"single-GPU library; sharding is described in DESIGN.md)", file=sys.stderr)
+              f"single-GPU library; it has no multi-GPU code)", file=sys.stderr)
         sys.exit(2)
     import numpy as np  # noqa: F401
     import torch

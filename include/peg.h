@@ -5,11 +5,9 @@
  * dense routing-map compaction.
  *
  * Sources (web pages; cited by title and section):
- *   [BIN]  "Build Triton-Ascend Binned MoE Routing" (SKILL.md of
- *          build-triton-ascend-binned-moe-routing): Goal, Workflow,
+ *   [BIN]  "Build Triton-Ascend Binned MoE Routing": Goal, Workflow,
  *          Implementation Pattern, Ascend Guardrails, Verification.
- *   [PAD]  "Build Triton-Ascend Padded MoE Routing" (SKILL.md of
- *          build-triton-ascend-padded-moe-routing): same sections.
+ *   [PAD]  "Build Triton-Ascend Padded MoE Routing": same sections.
  *   [MOK]  "core.transformer.moe.megakernel.mok.route_adapter" (Megatron-Core
  *          API page): RoutingMapToIndices, routing_map_to_mok_inputs.
  *   [FMD]  "Fused MoE Dispatch (Triton, universal)": the pipeline diagram
