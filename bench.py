@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
     ap.add_argument("--no-router", action="store_true", help="skip timing the router gating")
+    ap.add_argument("--graph", action="store_true",
+                    help="region 1 replays one captured HIP graph per input copy instead of launching the calls")
     ap.add_argument("--from-logits", action="store_true",
                     help="start each step from the router scores: gating fused with route_prep replaces route_prep "
                          "(workloads with router scores)")
@@ -101,25 +103,27 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
 
 
-def copy_ceiling(torch, hip, stream):
+def copy_ceiling(torch, hip, tstream):
     """Device-to-device copy rate of this GPU (torch's copy of 1 GiB between
     two buffers, read + write bytes per second), timed with HIP events: the
     achievable ceiling that a kernel moving as many bytes as it reads can
     reach."""
     n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-    for _ in range(2):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    ms = []
-    for _ in range(5):
-        a, b = hip.create(), hip.create()
-        hip.record(a, stream)
-        dst.copy_(src)
-        hip.record(b, stream)
+    stream = ctypes.c_void_p(tstream.cuda_stream)
+    with torch.cuda.stream(tstream):
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        for _ in range(2):
+            dst.copy_(src)
         torch.cuda.synchronize()
-        ms.append(hip.elapsed_ms(a, b))
+        ms = []
+        for _ in range(5):
+            a, b = hip.create(), hip.create()
+            hip.record(a, stream)
+            dst.copy_(src)
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            ms.append(hip.elapsed_ms(a, b))
     ms.sort()
     del src, dst
     return round(2 * n / (ms[len(ms) // 2] / 1e3) / 1e9, 1)
@@ -410,20 +414,41 @@ def main():
     per_set = (wl.T * wl.H * s) * 3 + sz["R"] * wl.H * s * (1 if args.no_backward else 2)
     sets = args.sets or max(2, min(16, math.ceil(2 * 2 ** 30 / per_set)))
     log(f"R={sz['R']} N={sz['N']} U={sz['U']} step bytes={bytes_step / 1e6:.1f} MB, {sets} input copies")
-    steps_obj = [Step(peg, torch, wl, dev, host) for _ in range(sets)]
+    # every call goes to one stream of its own (default priority), which a
+    # graph capture can also use
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        steps_obj = [Step(peg, torch, wl, dev, host) for _ in range(sets)]
     torch.cuda.synchronize()
 
     names = steps_obj[0].order
     for i in range(args.warmup):
         steps_obj[i % sets].run()
     torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        graphs = []
+        for st in steps_obj:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                st.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(min(args.warmup, sets)):
+            graphs[i % sets].replay()
+        torch.cuda.synchronize()
 
     # Timed region 1 (the headline): K whole steps back to back, nothing else
     # on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        steps_obj[(args.warmup + i) % sets].run()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            if graphs:
+                graphs[(args.warmup + i) % sets].replay()
+            else:
+                steps_obj[(args.warmup + i) % sets].run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -484,7 +509,7 @@ def main():
             extras[name]["traffic"] = traffic_for("backward", wl.name)
         if name in ("router_topk", "route_prep_logits"):
             extras[name]["tokens_per_s"] = round(wl.T / (avg / 1e3), 1)
-    copy_GBps = copy_ceiling(torch, HipEvents(), steps_obj[0].stream) if not args.no_events else None
+    copy_GBps = copy_ceiling(torch, HipEvents(), stream) if not args.no_events else None
     if roofline and copy_GBps:
         roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / copy_GBps, 4)
     cpu = None
@@ -502,6 +527,7 @@ def main():
                    "layout": "binned" if wl.layout == W.BINNED else "padded",
                    "capacity": wl.capacity or None, "pad_multiple": wl.pad_multiple or None,
                    "compaction": wl.routing_map is not None, "input_copies": sets, "from_logits": args.from_logits,
+        "launch": "hip graph per step" if args.graph else "calls",
                    "rows": sz["R"], "kept": sz["N"], "tokens_with_route": sz["U"]},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "routed_tokens_per_s": round(wl.T / (ms_step / 1e3), 1),
