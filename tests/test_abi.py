@@ -204,3 +204,18 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         peg.route_prep(torch.zeros((4, 2), dtype=torch.int32), 4, capacity=2)
+
+
+def test_plain_c_consumer(tmp_path):
+    """The header compiles as strict C99 and the library links from C."""
+    import subprocess
+    src = os.path.join(ROOT, "tests", "c", "abi_check.c")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(peg.LIB_PATH)
+    lib = os.path.basename(peg.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", str(exe), "-L", libdir, "-l:" + lib, "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert "abi_check ok" in out.stdout
+
