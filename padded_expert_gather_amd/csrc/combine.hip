@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     constexpr int N = L::N;
     constexpr int KB = KR < kKBatch ? KR : kKBatch;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = (int64_t)blockIdx.x * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+    const int64_t t = xcd_block(blockIdx.x, gridDim.x) * TokenMap<WPT>::kTokensPerBlock + w / WPT;
     if (t >= T) return;  // no barrier in this kernel
     const int lane = lane_id();
     const int64_t c_begin = (w % WPT) * slice;
@@ -180,6 +180,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
         }
         tblock = role_index;
     }
+    tblock = xcd_block(tblock, token_blocks);
     __shared__ float red[NW][KR];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int TPB = TokenMap<WPT>::kTokensPerBlock;

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
         // ---------------- token row -> its expert rows ----------------
         // (no barrier in this part: waves run independently)
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-        const int64_t t = role_index * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+        const int64_t t = xcd_block(role_index, token_blocks) * TokenMap<WPT>::kTokensPerBlock + w / WPT;
         if (t >= T) return;
         const int lane = lane_id();
         const int64_t c_begin = (w % WPT) * slice;

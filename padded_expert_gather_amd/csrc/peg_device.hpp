@@ -246,6 +246,26 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+// Blocks of a launch go to the 8 XCDs in turn (block b to XCD b % 8). With
+// PEG_XCD_REMAP the token kernels give XCD x one contiguous run of their n
+// token blocks instead of every 8th, so that each XCD's L2 and address
+// translation see 1/8 of the rows. xcd_block(b, n) is a bijection on [0, n).
+// Measured and left off: it costs 1-10% at T4096 H4096 and up to 2x at
+// T32768 H3584 (a contiguous run of rows per XCD concentrates the
+// concurrent accesses on fewer memory channels).
+#ifndef PEG_XCD_REMAP
+#define PEG_XCD_REMAP 0
+#endif
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t n) {
+#if PEG_XCD_REMAP
+    const int64_t x = b & 7, i = b >> 3, base = n >> 3, rem = n & 7;
+    return x * base + (x < rem ? x : rem) + i;
+#else
+    (void)n;
+    return b;
+#endif
+}
+
 // Value of lane 63 in every lane.
 __device__ __forceinline__ int last_lane(int v) { return __builtin_amdgcn_readlane(v, kWave - 1); }
 
