@@ -229,6 +229,31 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
                             if (c < c_end) v[kk][u] = stream_load<VEC>(src, c);
                         }
                     }
+                    if constexpr (DY != 0) {
+                        // dy rows need only dout: they are stored while the
+                        // expert rows loaded above are still in flight
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const int64_t c = c0 + u * kWave + lane;
+                            if (c >= c_end) continue;
+                            float g[N];
+                            if constexpr (DY == 2) L::unpack(gv[u], g);
+#pragma unroll
+                            for (int kk = 0; kk < KB; ++kk) {
+                                const int r = r8[kb + kk];
+                                if (r < 0 || r >= dy_rows) continue;
+                                uint8_t* drow = dy + (int64_t)r * row_bytes;
+                                if constexpr (DY == 1) {
+                                    stream_store<VEC>(drow, c, gv[u]);
+                                } else {
+                                    float o[N];
+#pragma unroll
+                                    for (int i = 0; i < N; ++i) o[i] = w8[kb + kk] * g[i];
+                                    stream_store<VEC>(drow, c, L::pack(o));
+                                }
+                            }
+                        }
+                    }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int64_t c = c0 + u * kWave + lane;
@@ -237,25 +262,11 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
                         L::unpack(gv[u], g);
 #pragma unroll
                         for (int kk = 0; kk < KB; ++kk) {
-                            const int r = r8[kb + kk];
-                            if (r < 0) continue;
+                            if (r8[kb + kk] < 0) continue;
                             float f[N];
                             L::unpack(v[kk][u], f);
 #pragma unroll
                             for (int i = 0; i < N; ++i) acc[kb + kk] = fmaf(f[i], g[i], acc[kb + kk]);
-                            if constexpr (DY != 0) {
-                                if (r < dy_rows) {
-                                    uint8_t* drow = dy + (int64_t)r * row_bytes;
-                                    if constexpr (DY == 1) {
-                                        stream_store<VEC>(drow, c, gv[u]);
-                                    } else {
-                                        float o[N];
-#pragma unroll
-                                        for (int i = 0; i < N; ++i) o[i] = w8[kb + kk] * g[i];
-                                        stream_store<VEC>(drow, c, L::pack(o));
-                                    }
-                                }
-                            }
                         }
                     }
                 }
