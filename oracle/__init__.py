@@ -59,6 +59,8 @@ def load_library(path):
     lib.pego_routing_map_compact.restype = c_int32
     lib.pego_routing_map_compact_backward.argtypes = [f32p, i32p, c_int64, c_int32, c_int32, f32p]
     lib.pego_routing_map_compact_backward.restype = c_int32
+    lib.pego_assignment_rows_windows.argtypes = [c_int64, c_int32, c_int32, i32p, i32p, i32p, i32p, i32p, i32p]
+    lib.pego_assignment_rows_windows.restype = c_int32
     lib.pego_router_topk.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, i32p, f32p]
     lib.pego_router_topk.restype = c_int32
     lib.pego_validate_routing.argtypes = [i32p, i32p, i32p, i32p, c_int64, c_int32, c_int32, c_int64]
@@ -156,6 +158,21 @@ def assignment_rows(r, layout, capacity=None):
                                       _p(out, c_int32))
     if rc != 0:
         raise ValueError("oracle assignment_rows refused its arguments")
+    return out
+
+
+def assignment_rows_windows(r, row_base, row_limit):
+    """Row of every assignment when expert e owns rows [row_base[e],
+    row_limit[e]) (-1: no route, or past the window)."""
+    total = r.T * r.K
+    out = np.empty(total, np.int32)
+    base = _c(row_base, np.int32)
+    limit = _c(row_limit, np.int32)
+    rc = _load().pego_assignment_rows_windows(r.T, r.K, r.E, _p(r.indices, c_int32), _p(r.bin_ids, c_int32),
+                                              _p(r.bins, c_int32), _p(base, c_int32), _p(limit, c_int32),
+                                              _p(out, c_int32))
+    if rc != 0:
+        raise ValueError("oracle assignment_rows_windows refused its arguments")
     return out
 
 

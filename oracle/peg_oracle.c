@@ -240,6 +240,38 @@ int pego_assignment_rows(int64_t T, int32_t K, int32_t E, int32_t layout, int32_
     return 0;
 }
 
+/*
+ * Rows of every assignment id when each expert owns a caller-given window of
+ * rows [row_base[e], row_limit[e]): the Implementation Pattern's row formula
+ * of [BIN] (segment start e*C plus the offset inside the expert, dropped past
+ * the segment's C rows) and of [PAD] (padded segment start plus offset), with
+ * the segment start and end supplied per expert. Sorted position i of expert
+ * e = bin_ids[i] has offset i - start(e); its row is row_base[e] + offset if
+ * that is below row_limit[e], else the assignment is dropped (-1).
+ * (Used for one shard of a token-sharded batch: the windows then start where
+ * the earlier shards' assignments of each expert end.)
+ */
+int pego_assignment_rows_windows(int64_t T, int32_t K, int32_t E, const int32_t* indices,
+                                 const int32_t* bin_ids, const int32_t* bins,
+                                 const int32_t* row_base, const int32_t* row_limit,
+                                 int32_t* rows_out) {
+    if (T < 0 || K < 1 || E < 1 || !indices || !bin_ids || !bins || !row_base || !row_limit || !rows_out)
+        return -1;
+    int64_t total = T * (int64_t)K;
+    for (int64_t a = 0; a < total; ++a) rows_out[a] = -1;
+    int64_t n = valid_count(bins, E, total);
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t expert = bin_ids[i];
+        if (expert < 0 || expert >= E) return -1;
+        int64_t start = expert == 0 ? 0 : bins[expert - 1];
+        int64_t row = (int64_t)row_base[expert] + (i - start);
+        int32_t a = indices[i];
+        if (a < 0 || a >= total) return -1;
+        rows_out[a] = row < row_limit[expert] ? (int32_t)row : -1;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Gathers.                                                                 */
 /* ------------------------------------------------------------------------ */

@@ -47,6 +47,12 @@ int pego_assignment_rows(int64_t T, int32_t K, int32_t E, int32_t layout, int32_
                          const int32_t* indices, const int32_t* bin_ids, const int32_t* bins,
                          const int32_t* padded_bins, int32_t* rows_out);
 
+/* Rows within caller-given per-expert windows [row_base[e], row_limit[e]). */
+int pego_assignment_rows_windows(int64_t T, int32_t K, int32_t E, const int32_t* indices,
+                                 const int32_t* bin_ids, const int32_t* bins,
+                                 const int32_t* row_base, const int32_t* row_limit,
+                                 int32_t* rows_out);
+
 int pego_gather(const void* x, int64_t T, int64_t row_bytes, int32_t K, int32_t E,
                 int32_t layout, int32_t capacity, const int32_t* indices,
                 const int32_t* bin_ids, const int32_t* bins, const int32_t* padded_bins,

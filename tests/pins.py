@@ -482,6 +482,41 @@ def pin_combine_backward(o):
                                                             rows=sample).view(np.uint8), dy[sample].view(np.uint8))
 
 
+def pin_windows(o):
+    """Rows within per-expert windows vs brute-force enumeration: windows
+    [e*C, (e+1)*C) give the binned rows, windows [pstart(e), padded_bins[e])
+    the padded rows, and a batch cut into contiguous token shards, each
+    routed on its own with windows that start where the earlier shards'
+    assignments of each expert end, reproduces the binned rows of the whole
+    batch."""
+    rng = np.random.default_rng(83)
+    for top, w, E in _tiny_cases():
+        T, K = top.shape
+        r = o.route_prep(top, E)
+        for C in (1, 2, 5):
+            want, _ = brute_rows(top, E, W.BINNED, capacity=C)
+            base = np.arange(E, dtype=np.int32) * C
+            got = o.assignment_rows_windows(r, base, base + C)
+            assert np.array_equal(got, want), "windows = binned rows"
+        m = 3
+        rp = o.route_prep(top, E, pad_multiple=m)
+        want, _ = brute_rows(top, E, W.PADDED, pad_multiple=m)
+        pstart = np.concatenate([[0], rp.padded_bins[:-1]]).astype(np.int32)
+        assert np.array_equal(o.assignment_rows_windows(rp, pstart, rp.padded_bins), want), "windows = padded rows"
+        if T >= 3:
+            C = 2
+            want, _ = brute_rows(top, E, W.BINNED, capacity=C)
+            cuts = sorted(rng.choice(np.arange(1, T), size=2, replace=False).tolist())
+            taken = np.zeros(E, np.int64)
+            got = []
+            for lo, hi in zip([0] + cuts, cuts + [T]):
+                rs = o.route_prep(top[lo:hi], E)
+                base = (np.arange(E) * C + taken).astype(np.int32)
+                got.append(o.assignment_rows_windows(rs, base, (np.arange(E, dtype=np.int32) + 1) * C))
+                taken += rs.tokens_per_expert
+            assert np.array_equal(np.concatenate(got), want), "sharded windows = rows of the whole batch"
+
+
 # ----------------------------------------------------------------------------
 # Routing-map compaction.
 # ----------------------------------------------------------------------------
@@ -640,5 +675,5 @@ def pin_validate(o):
 ALL_PINS = [pin_bf16_rounding, pin_f16_rounding, pin_widening, pin_route_prep_numpy, pin_route_prep_exhaustive,
             pin_route_prep_invariants, pin_golden, pin_gather_numpy, pin_gather_bits_and_identity,
             pin_scatter_closed_form, pin_scatter_random_y, pin_wgrad_autograd, pin_wgrad_closed_form,
-            pin_sampled_tokens, pin_combine_backward, pin_compaction, pin_router_selection,
+            pin_sampled_tokens, pin_combine_backward, pin_windows, pin_compaction, pin_router_selection,
             pin_router_weights_library, pin_router_matches_workload_router, pin_router_closed_forms, pin_validate]

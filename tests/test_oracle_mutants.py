@@ -61,6 +61,10 @@ MUTANTS = [
     ("router_normalize_ignored", "(float)(normalize ? p[k] / sel : p[k])", "(float)p[k]", 0),
     ("router_selected_sum_first_only", "for (int32_t k = 0; k < K; ++k) sel += p[k];",
      "for (int32_t k = 0; k < 1; ++k) sel += p[k];", 0),
+    ("windows_limit_inclusive", "rows_out[a] = row < row_limit[expert] ? (int32_t)row : -1;",
+     "rows_out[a] = row <= row_limit[expert] ? (int32_t)row : -1;", 0),
+    ("windows_base_ignored", "int64_t row = (int64_t)row_base[expert] + (i - start);",
+     "int64_t row = (int64_t)row_base[0] + (i - start);", 0),
     ("validate_no_duplicates", "if (seen[a]) flags |= FLAG_INDICES;", "(void)seen[a];", 0),
     ("validate_expected_off", "if (bins[e] <= i) ++expect;", "if (bins[e] < i) ++expect;", 0),
 ]
