@@ -237,6 +237,48 @@ peg_status peg_combine_backward(const void* y, const void* dout, const float* we
                                 const int32_t* padded_bins, const int32_t* slot_row, void* dy, int64_t dy_rows,
                                 float* wgrad, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * peg_route_prep_windows - the routing preparation of peg_route_prep with
+ * each expert's rows in a caller-given window [row_base[e], row_limit[e]).
+ * [BIN]/[PAD] Workflow steps 1-2 (stable sort by expert, inclusive bins) and
+ * the Implementation Pattern's row formula (segment start + offset inside the
+ * expert, dropped past the segment's end) with the segment start and end
+ * supplied per expert.
+ *
+ * indices, bin_ids, tokens_per_expert and bins are exactly those of
+ * peg_route_prep for this batch. slot_row[a] = row_base[e] + offset of a
+ * inside expert e (ascending assignment id), or -1 if that is at or past
+ * row_limit[e] (dropped) or a has no route. Windows [e*C, (e+1)*C) give the
+ * binned layout; for one shard of a batch cut into contiguous token ranges,
+ * windows starting at e*C + (assignments of e in the earlier shards) place
+ * the shard's rows, and drop its assignments, exactly as one call over the
+ * whole batch would (the earlier shards' counts come from their
+ * tokens_per_expert: an all-gather of E counts per shard and a prefix sum).
+ *   row_base, row_limit [E] int32 device, 0 <= row_base[e];
+ *   other arguments as for peg_route_prep; ws: peg_workspace_bytes(T, K, E).
+ * Errors: NULL_ARG, BAD_SHAPE, WORKSPACE, LAUNCH.
+ */
+peg_status peg_route_prep_windows(const int32_t* top_experts, int64_t T, int32_t K, int32_t E,
+                                  const int32_t* row_base, const int32_t* row_limit, int32_t* indices,
+                                  int32_t* bin_ids, int32_t* tokens_per_expert, int32_t* bins,
+                                  int32_t* slot_row, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * peg_gather_rows - dispatch by a row map alone: out[slot_row[a]] =
+ * x[a / K] for every assignment a with 0 <= slot_row[a] < out_rows (raw
+ * bytes). [BIN] Workflow step 3 / [PAD] Workflow step 4 (copy each kept
+ * token row to its expert row) without the zero-fill of unused rows: rows no
+ * assignment maps to are left as they are, for a caller that assembles one
+ * expert tensor from several calls (shards) and clears it itself.
+ * A row at or past out_rows is skipped and sets PEG_FLAG_OUT_ROWS in
+ * *err_flag (if err_flag != NULL).
+ *   x [T, H] of dtype; slot_row [T*K] int32 device; out [out_rows, H].
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, ALIGNMENT, LAUNCH.
+ */
+peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K,
+                           const int32_t* slot_row, void* out, int64_t out_rows, uint32_t* err_flag,
+                           void* stream);
+
 /* Gating functions of peg_router_topk. */
 #define PEG_GATING_SOFTMAX 0
 #define PEG_GATING_SIGMOID 1

@@ -8,7 +8,8 @@ without a GPU the calls raise.
 
 Functions (same names as the C entry points without the ``peg_`` prefix):
   route_prep, gather_binned, gather_padded, scatter_combine, wgrad,
-  combine_backward, router_topk, route_prep_logits, routing_map_compact,
+  combine_backward, router_topk, route_prep_logits, route_prep_windows,
+  gather_rows, routing_map_compact,
   routing_map_compact_backward, validate_routing.
 """
 import ctypes
@@ -66,6 +67,8 @@ def _load():
         "peg_combine_backward": ([P, P, P, c_int32, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, P, P, P, P,
                                   P, P, c_int64, P, P, c_size_t, P], st),
         "peg_router_topk": ([P, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, P, P, P], st),
+        "peg_route_prep_windows": ([P, c_int64, c_int32, c_int32, P, P, P, P, P, P, P, P, c_size_t, P], st),
+        "peg_gather_rows": ([P, c_int32, c_int64, c_int64, c_int32, P, P, c_int64, P, P], st),
         "peg_route_prep_logits": ([P, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                    c_int32, P, P, P, P, P, P, P, P, P, c_size_t, P], st),
         "peg_routing_map_compact": ([P, c_int32, P, c_int64, c_int32, c_int32, P, P, P], st),
@@ -214,6 +217,53 @@ def route_prep_logits(logits, K, capacity=None, pad_multiple=None, gating=SOFTMA
                                            _ptr(ws), wsb, _stream(dev))
     _check(st, "route_prep_logits")
     return Routing(T, K, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins, padded, slot_row), top, w
+
+
+def route_prep_windows(top_experts, num_experts, row_base, row_limit, capacity=None, ws=None):
+    """route_prep with expert e's rows in [row_base[e], row_limit[e]) (int32
+    device tensors): same sorted arrays as route_prep, slot_row in the
+    windows. ``capacity`` (optional) tags the result as a binned layout of E
+    * capacity rows for the combine / wgrad calls that take it; its gaps are
+    the caller's (see gather_rows)."""
+    top = _dev(top_experts, "top_experts", torch.int32)
+    if top.dim() != 2:
+        raise ValueError("top_experts must be [T, K]")
+    T, K = top.shape
+    E = int(num_experts)
+    base = _dev(row_base, "row_base", torch.int32)
+    limit = _dev(row_limit, "row_limit", torch.int32)
+    if base.numel() != E or limit.numel() != E:
+        raise ValueError("row_base and row_limit must hold E values")
+    dev = top.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    indices = torch.empty(T * K, **i32)
+    bin_ids = torch.empty(T * K, **i32)
+    tpe = torch.empty(E, **i32)
+    bins = torch.empty(E, **i32)
+    slot_row = torch.empty(T * K, **i32)
+    ws, wsb = _ws(T, K, E, dev, ws)
+    with torch.cuda.device(dev):
+        st = _load().peg_route_prep_windows(_ptr(top), T, K, E, _ptr(base), _ptr(limit), _ptr(indices),
+                                            _ptr(bin_ids), _ptr(tpe), _ptr(bins), _ptr(slot_row), _ptr(ws), wsb,
+                                            _stream(dev))
+    _check(st, "route_prep_windows")
+    return Routing(T, K, E, BINNED, capacity, None, indices, bin_ids, tpe, bins, None, slot_row)
+
+
+def gather_rows(x, slot_row, K, out, err_flag=None):
+    """out[slot_row[a]] = x[a // K] for every a with 0 <= slot_row[a] < rows
+    of out; no other row of out is written."""
+    x = _dev(x, "x")
+    slot_row = _dev(slot_row, "slot_row", torch.int32)
+    out = _dev(out, "out", x.dtype)
+    T, H = x.shape
+    if slot_row.numel() != T * int(K) or out.shape[1] != H:
+        raise ValueError("slot_row must hold T*K rows and out must have rows of H elements")
+    with torch.cuda.device(x.device):
+        st = _load().peg_gather_rows(_ptr(x), _dtype_code(x, "x"), T, H, int(K), _ptr(slot_row), _ptr(out),
+                                     out.shape[0], _ptr(err_flag), _stream(x.device))
+    _check(st, "gather_rows")
+    return out
 
 
 def _slot(r, use_slot_row):

@@ -199,3 +199,45 @@ PEG_API peg_status peg_gather_padded(const void* x, int32_t dtype, int64_t T, in
     return gather_common(x, dtype, T, H, K, E, PEG_PADDED, 0, indices, bin_ids, bins, padded_bins, slot_row, out,
                          out_rows, err_flag, ws, ws_bytes, stream);
 }
+
+PEG_API peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K,
+                                   const int32_t* slot_row, void* out, int64_t out_rows, uint32_t* err_flag,
+                                   void* stream) {
+    if (!dtype_ok(dtype)) return PEG_ERR_BAD_DTYPE;
+    if (T < 0 || H < 1 || K < 1 || K > PEG_MAX_EXPERTS || T > kMaxAssign / K) return PEG_ERR_BAD_SHAPE;
+    if (out_rows < 0 || out_rows > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(dtype);
+    if (H > (int64_t(1) << 40) / eb) return PEG_ERR_BAD_SHAPE;
+    if (T > 0 && (!x || !slot_row || (!out && out_rows > 0))) return PEG_ERR_NULL_ARG;
+    if (!aligned(x, eb) || !aligned(out, eb)) return PEG_ERR_ALIGNMENT;
+    const int64_t row_bytes = H * eb;
+    const int vec = pick_vec(row_bytes, eb, x, out);
+    if (vec == 0) return PEG_ERR_ALIGNMENT;
+    if (T == 0) return PEG_OK;
+    const int64_t nch = row_bytes / vec;
+    const int wpt = gather_wpt(nch);
+    const int64_t tb = token_blocks(T, wpt);
+    const int64_t slice = wave_slice(nch, wpt);
+    const int u = lanes_per_pass(slice);
+    // no gap blocks: the grid holds token blocks only, so the gap arguments
+    // are never read
+    const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, slice, K, slot_row, out_rows, PEG_BINNED, 1, 1,
+                       nullptr, nullptr, T, tb, err_flag};
+    const dim3 grid((unsigned)tb);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (wpt == 2) {
+        switch (vec) {
+            case 16: return gather_launch<16, 2>(u, grid, s, a);
+            case 8: return gather_launch<8, 2>(u, grid, s, a);
+            case 4: return gather_launch<4, 2>(u, grid, s, a);
+            default: return gather_launch<2, 2>(u, grid, s, a);
+        }
+    }
+    switch (vec) {
+        case 16: return gather_launch<16, 4>(u, grid, s, a);
+        case 8: return gather_launch<8, 4>(u, grid, s, a);
+        case 4: return gather_launch<4, 4>(u, grid, s, a);
+        default: return gather_launch<2, 4>(u, grid, s, a);
+    }
+}
+

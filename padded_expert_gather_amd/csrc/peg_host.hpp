@@ -111,7 +111,9 @@ inline size_t ws_need(int64_t T, int32_t K, int32_t E) {
     int64_t ntiles = prep_tiles(total, E);
     const int64_t nfused = K > 0 ? tiles_of(total, fused_items(total, K, E)) : 0;
     if (nfused > ntiles) ntiles = nfused;
-    size_t tile_counts = (size_t)ntiles * (size_t)E * 4;  // route_prep (plain or fused with the gating)
+    // route_prep (plain or fused with the gating); with row windows the
+    // padded bins of E experts sit in front of the table
+    size_t tile_counts = (size_t)ntiles * (size_t)E * 4 + (((size_t)E * 4 + 255) & ~size_t(255));
     size_t slots = (size_t)total * 4;                                   // slot_row rebuild
     size_t bitmap = (size_t)((total + 31) / 32) * 4 + 64;               // validation
     size_t need = tile_counts;

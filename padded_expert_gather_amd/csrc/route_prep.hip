@@ -501,6 +501,79 @@ static int small_items(int64_t total, int32_t E) {
     return items;
 }
 
+// Everything of peg_route_prep after its argument checks; counts: the
+// workspace.
+static peg_status prep_dispatch(const int32_t* top_experts, int64_t total, int32_t E, int32_t layout,
+                                int32_t capacity, int32_t pad_multiple, int32_t* indices, int32_t* bin_ids,
+                                int32_t* tokens_per_expert, int32_t* bins, int32_t* padded_bins, int32_t* slot_row,
+                                int32_t* counts, hipStream_t s) {
+    switch (small_items(total, E)) {
+        case 1: return prep_small<1>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 2: return prep_small<2>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 4: return prep_small<4>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 8: return prep_small<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                     tokens_per_expert, bins, padded_bins, slot_row, s);
+        case 16: return prep_small<16>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
+                                       tokens_per_expert, bins, padded_bins, slot_row, s);
+        default: break;
+    }
+    switch (tiled_items(total, E)) {
+#define PEG_TILED(I)                                                                                             \
+    case I:                                                                                                      \
+        return prep_tiled<I>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,            \
+                             tokens_per_expert, bins, padded_bins, slot_row, counts, s)
+        PEG_TILED(16);
+        PEG_TILED(8);
+        PEG_TILED(4);
+        PEG_TILED(2);
+        PEG_TILED(1);
+#undef PEG_TILED
+        default: return PEG_ERR_BAD_SHAPE;
+    }
+}
+
+peg_status prep_place(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
+                      int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
+                      int32_t* padded_bins, int32_t* slot_row, int32_t* counts, int items, hipStream_t s) {
+    switch (items) {
+#define PEG_PLACE(I)                                                                                             \
+    case I:                                                                                                      \
+        return place_tiles<I>(top, total, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins,        \
+                              padded_bins, slot_row, counts, s)
+        PEG_PLACE(16);
+        PEG_PLACE(8);
+        PEG_PLACE(4);
+        PEG_PLACE(2);
+        PEG_PLACE(1);
+#undef PEG_PLACE
+        default: return PEG_ERR_BAD_SHAPE;
+    }
+}
+
+// Rows within caller-given windows: slot_row arrives holding each
+// assignment's sorted position (the routing of the padded layout with a
+// multiple of 1, whose segments are the real ones), and leaves holding
+// row_base[e] + (position - start(e)), or -1 past row_limit[e].
+__global__ __launch_bounds__(kBlock) void windows_kernel(const int32_t* __restrict__ top, int64_t total, int32_t E,
+                                                         const int32_t* __restrict__ bins,
+                                                         const int32_t* __restrict__ row_base,
+                                                         const int32_t* __restrict__ row_limit,
+                                                         int32_t* __restrict__ slot_row) {
+    const int64_t a = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (a >= total) return;
+    const int e = top[a];
+    const int pos = slot_row[a];
+    int row = -1;
+    if ((unsigned)e < (unsigned)E && pos >= 0) {
+        const int64_t r = (int64_t)row_base[e] + (pos - (e ? bins[e - 1] : 0));
+        row = (r >= 0 && r < row_limit[e]) ? (int)r : -1;
+    }
+    slot_row[a] = row;
+}
+
 }  // namespace peg
 
 using namespace peg;
@@ -522,54 +595,30 @@ PEG_API peg_status peg_route_prep(const int32_t* top_experts, int64_t T, int32_t
     if (layout == PEG_PADDED && !padded_bins) return PEG_ERR_NULL_ARG;
     if (!ws) return PEG_ERR_WORKSPACE;
     if (ws_bytes < ws_need(T, K, E)) return PEG_ERR_WORKSPACE;
+    return prep_dispatch(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids, tokens_per_expert,
+                         bins, padded_bins, slot_row, reinterpret_cast<int32_t*>(ws),
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+PEG_API peg_status peg_route_prep_windows(const int32_t* top_experts, int64_t T, int32_t K, int32_t E,
+                                          const int32_t* row_base, const int32_t* row_limit, int32_t* indices,
+                                          int32_t* bin_ids, int32_t* tokens_per_expert, int32_t* bins,
+                                          int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || K < 1 || E < 1 || E > PEG_MAX_EXPERTS) return PEG_ERR_BAD_SHAPE;
+    if (T > kMaxAssign / K) return PEG_ERR_BAD_SHAPE;
+    const int64_t total = T * (int64_t)K;
+    if (!bins || (total > 0 && (!top_experts || !indices || !bin_ids || !slot_row || !row_base || !row_limit)))
+        return PEG_ERR_NULL_ARG;
+    if (!ws || ws_bytes < ws_need(T, K, E)) return PEG_ERR_WORKSPACE;
+    // the padded bins of the multiple-1 routing go first in the workspace,
+    // the routing preparation's own scratch after them
+    const size_t pb_bytes = ((size_t)E * sizeof(int32_t) + 255) & ~size_t(255);
+    int32_t* pb = reinterpret_cast<int32_t*>(ws);
+    int32_t* counts = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(ws) + pb_bytes);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    switch (small_items(total, E)) {
-        case 1: return prep_small<1>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                                     tokens_per_expert, bins, padded_bins, slot_row, s);
-        case 2: return prep_small<2>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                                     tokens_per_expert, bins, padded_bins, slot_row, s);
-        case 4: return prep_small<4>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                                     tokens_per_expert, bins, padded_bins, slot_row, s);
-        case 8: return prep_small<8>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                                     tokens_per_expert, bins, padded_bins, slot_row, s);
-        case 16: return prep_small<16>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,
-                                       tokens_per_expert, bins, padded_bins, slot_row, s);
-        default: break;
-    }
-    int32_t* counts = reinterpret_cast<int32_t*>(ws);
-    switch (tiled_items(total, E)) {
-#define PEG_TILED(I)                                                                                             \
-    case I:                                                                                                      \
-        return prep_tiled<I>(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids,            \
-                             tokens_per_expert, bins, padded_bins, slot_row, counts, s)
-        PEG_TILED(16);
-        PEG_TILED(8);
-        PEG_TILED(4);
-        PEG_TILED(2);
-        PEG_TILED(1);
-#undef PEG_TILED
-        default: return PEG_ERR_BAD_SHAPE;
-    }
+    PEG_CHECK(prep_dispatch(top_experts, total, E, PEG_PADDED, 0, 1, indices, bin_ids, tokens_per_expert, bins, pb,
+                            slot_row, counts, s));
+    if (total == 0) return PEG_OK;
+    return launch(windows_kernel, dim3((unsigned)((total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, top_experts,
+                  total, E, bins, row_base, row_limit, slot_row);
 }
-
-namespace peg {
-
-peg_status prep_place(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
-                      int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
-                      int32_t* padded_bins, int32_t* slot_row, int32_t* counts, int items, hipStream_t s) {
-    switch (items) {
-#define PEG_PLACE(I)                                                                                             \
-    case I:                                                                                                      \
-        return place_tiles<I>(top, total, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins,        \
-                              padded_bins, slot_row, counts, s)
-        PEG_PLACE(16);
-        PEG_PLACE(8);
-        PEG_PLACE(4);
-        PEG_PLACE(2);
-        PEG_PLACE(1);
-#undef PEG_PLACE
-        default: return PEG_ERR_BAD_SHAPE;
-    }
-}
-
-}  // namespace peg

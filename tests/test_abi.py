@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
 
@@ -183,6 +183,34 @@ def test_route_prep_logits_checks(lib):
     assert call(ws=None) == WORKSPACE
     assert call(wsb=8) == WORKSPACE
     assert call(w=_p(FAKE + 1)) == ALIGNMENT
+
+
+def test_windows_and_gather_rows_checks(lib):
+    f = lib.peg_route_prep_windows
+
+    def win(T=4, K=2, E=4, base=_p(FAKE), limit=_p(FAKE), idx=_p(FAKE), bins=_p(FAKE), sr=_p(FAKE), ws=_p(FAKE),
+            wsb=1 << 20):
+        return f(_p(FAKE), T, K, E, base, limit, idx, _p(FAKE), None, bins, sr, ws, wsb, None)
+
+    assert win(E=0) == BAD_SHAPE
+    assert win(K=0) == BAD_SHAPE
+    assert win(base=None) == NULL_ARG
+    assert win(limit=None) == NULL_ARG
+    assert win(sr=None) == NULL_ARG
+    assert win(bins=None) == NULL_ARG
+    assert win(ws=None) == WORKSPACE
+    assert win(wsb=16) == WORKSPACE
+    g = lib.peg_gather_rows
+
+    def gr(x=_p(FAKE), dt=1, T=4, H=8, K=2, sr=_p(FAKE), out=_p(FAKE), rows=16):
+        return g(x, dt, T, H, K, sr, out, rows, None, None)
+
+    assert gr(dt=4) == BAD_DTYPE
+    assert gr(H=0) == BAD_SHAPE
+    assert gr(rows=-1) == BAD_SHAPE
+    assert gr(sr=None) == NULL_ARG
+    assert gr(x=_p(FAKE + 1)) == ALIGNMENT
+    assert gr(T=0, x=None, sr=None) == OK
 
 
 def test_compaction_and_validate_checks(lib):
