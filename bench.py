@@ -104,10 +104,10 @@ def copy_calibration(torch):
 
 
 def copy_ceiling(torch, hip, tstream):
-    """Device-to-device copy rate of this GPU (torch's copy of 1 GiB between
-    two buffers, read + write bytes per second), timed with HIP events: the
-    achievable ceiling that a kernel moving as many bytes as it reads can
-    reach."""
+    """Streaming rates of this GPU measured with torch's own kernels on 1 GiB
+    buffers, timed with HIP events (median of 5): device-to-device copy (read
+    + write bytes per second), fill (write only) and a float32 sum (read
+    only). Returns {"copy": GB/s, "write": GB/s, "read": GB/s}."""
     n = 1 << 30
     stream = ctypes.c_void_p(tstream.cuda_stream)
     with torch.cuda.stream(tstream):
@@ -116,17 +116,25 @@ def copy_ceiling(torch, hip, tstream):
         for _ in range(2):
             dst.copy_(src)
         torch.cuda.synchronize()
-        ms = []
-        for _ in range(5):
-            a, b = hip.create(), hip.create()
-            hip.record(a, stream)
-            dst.copy_(src)
-            hip.record(b, stream)
+        def timed(fn):
+            fn()
             torch.cuda.synchronize()
-            ms.append(hip.elapsed_ms(a, b))
-    ms.sort()
+            ms = []
+            for _ in range(5):
+                a, b = hip.create(), hip.create()
+                hip.record(a, stream)
+                fn()
+                hip.record(b, stream)
+                torch.cuda.synchronize()
+                ms.append(hip.elapsed_ms(a, b))
+            return median(ms) / 1e3
+
+        t_copy = timed(lambda: dst.copy_(src))
+        t_fill = timed(lambda: dst.fill_(3))
+        t_sum = timed(lambda: src.view(torch.float32).sum())
     del src, dst
-    return round(2 * n / (ms[len(ms) // 2] / 1e3) / 1e9, 1)
+    return {"copy": round(2 * n / t_copy / 1e9, 1), "write": round(n / t_fill / 1e9, 1),
+            "read": round(n / t_sum / 1e9, 1)}
 
 
 def median(xs):
@@ -509,9 +517,9 @@ def main():
             extras[name]["traffic"] = traffic_for("backward", wl.name)
         if name in ("router_topk", "route_prep_logits"):
             extras[name]["tokens_per_s"] = round(wl.T / (avg / 1e3), 1)
-    copy_GBps = copy_ceiling(torch, HipEvents(), stream) if not args.no_events else None
-    if roofline and copy_GBps:
-        roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / copy_GBps, 4)
+    ceilings = copy_ceiling(torch, HipEvents(), stream) if not args.no_events else None
+    if roofline and ceilings:
+        roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / ceilings["copy"], 4)
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -535,7 +543,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "copy_ceiling_GBps": copy_GBps,
+        "streaming_GBps": ceilings,
         "outside_step": extras,
         "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},
     }
