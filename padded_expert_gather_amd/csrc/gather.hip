@@ -41,10 +41,11 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
         // ---------------- token row -> its expert rows ----------------
         // (no barrier in this part: waves run independently)
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-        const int64_t t = xcd_block(role_index, token_blocks) * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+        const int64_t gw = xcd_block(role_index, token_blocks) * (kBlock / kWave) + w;  // wave of the launch
+        const int64_t t = gw / WPT;
         if (t >= T) return;
         const int lane = lane_id();
-        const int64_t c_begin = (w % WPT) * slice;
+        const int64_t c_begin = (gw % WPT) * slice;
         const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
         const int32_t* my_rows = slot_row + t * K;
         // rows of the token: wave-uniform loads (scalar unit), K <= 8 kept in SGPRs
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
             if (r >= out_rows) over = true;
             any |= r >= 0 && r < out_rows;
         }
-        if (over && err_flag && lane == 0 && w % WPT == 0) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
+        if (over && err_flag && lane == 0 && gw % WPT == 0) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
         if (!any) return;  // token fully dropped: its row is never read
         const uint8_t* src = x + t * row_bytes;
         for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
@@ -170,6 +171,16 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
             default: return gather_launch<2, 2>(u, grid, s, a);
         }
     }
+#if PEG_GATHER_WPT > 4
+    if (wpt == PEG_GATHER_WPT) {
+        switch (vec) {
+            case 16: return gather_launch<16, PEG_GATHER_WPT>(u, grid, s, a);
+            case 8: return gather_launch<8, PEG_GATHER_WPT>(u, grid, s, a);
+            case 4: return gather_launch<4, PEG_GATHER_WPT>(u, grid, s, a);
+            default: return gather_launch<2, PEG_GATHER_WPT>(u, grid, s, a);
+        }
+    }
+#endif
     switch (vec) {
         case 16: return gather_launch<16, 4>(u, grid, s, a);
         case 8: return gather_launch<8, 4>(u, grid, s, a);
@@ -233,6 +244,16 @@ PEG_API peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int6
             default: return gather_launch<2, 2>(u, grid, s, a);
         }
     }
+#if PEG_GATHER_WPT > 4
+    if (wpt == PEG_GATHER_WPT) {
+        switch (vec) {
+            case 16: return gather_launch<16, PEG_GATHER_WPT>(u, grid, s, a);
+            case 8: return gather_launch<8, PEG_GATHER_WPT>(u, grid, s, a);
+            case 4: return gather_launch<4, PEG_GATHER_WPT>(u, grid, s, a);
+            default: return gather_launch<2, PEG_GATHER_WPT>(u, grid, s, a);
+        }
+    }
+#endif
     switch (vec) {
         case 16: return gather_launch<16, 4>(u, grid, s, a);
         case 8: return gather_launch<8, 4>(u, grid, s, a);

@@ -50,11 +50,21 @@ inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, con
 #define PEG_GATHER_WPT_SPLIT 512  // rows of at most this many vectors: 2 waves per token
 #endif
 
-inline int gather_wpt(int64_t nch) { return nch <= PEG_GATHER_WPT_SPLIT ? 2 : 4; }
+// Waves per token of the gather: 2 up to PEG_GATHER_WPT_SPLIT vectors per
+// row, else 4; PEG_GATHER_WPT (8 or 16) overrides it, a token then spanning
+// 2 or 4 blocks. Measured: 8 or 16 waves win 3% on some rows (768 or 896
+// vectors) and lose 5-25% on others (448 and 512), so the default stays.
+#ifndef PEG_GATHER_WPT
+#define PEG_GATHER_WPT 0
+#endif
+inline int gather_wpt(int64_t nch) {
+    if (PEG_GATHER_WPT > 0) return PEG_GATHER_WPT;
+    return nch <= PEG_GATHER_WPT_SPLIT ? 2 : 4;
+}
 
 template <int WPT>
 struct TokenMap {
-    static_assert(WPT == 1 || WPT == 2 || WPT == 4, "waves per token must be 1, 2 or 4");
+    static_assert(WPT == 1 || WPT == 2 || WPT == 4 || WPT == 8 || WPT == 16, "waves per token: 1 to 16");
     static constexpr int kTokensPerBlock = (kBlock / 64) / WPT;
 };
 
@@ -73,9 +83,12 @@ inline int lanes_per_pass(int64_t slice) {
     return p <= 1 ? 1 : (p <= 2 ? 2 : 4);
 }
 
+// Blocks for T tokens at wpt waves per token (wpt > 4: a token spans
+// wpt / 4 blocks).
 inline int64_t token_blocks(int64_t T, int wpt) {
-    const int64_t per = (kBlock / 64) / wpt;
-    return (T + per - 1) / per;
+    const int64_t waves = T * wpt;
+    const int64_t per = kBlock / 64;
+    return (waves + per - 1) / per;
 }
 
 // Tiles of the routing preparation: 256 threads x ITEMS assignments. The
