@@ -187,3 +187,23 @@ def test_large_config(cid):
     assert_close(to_host(dyg[torch.from_numpy(sample).to(DEV)]), dyo_s,
                  np.abs(W.to_f32(dyo_s, wl.dtype).astype(np.float64)), wl.dtype, "backward dy sample")
     print(f"[config {cid}] done", flush=True)
+
+
+@pytest.mark.parametrize("cid,seed", [(c, s) for c in (3, 4, 5) for s in (1, 2, 3, 4)])
+def test_large_config_routing_seeds(cid, seed):
+    """Workloads 3-5, seeds 1-4: the routing at full size (compaction for 4)
+    bit for bit, and a gather of narrow rows (H = 40) through it, every row
+    checked against its token (full-width rows are covered by seed 0)."""
+    print(f"[config {cid} seed {seed}] routing", flush=True)
+    wl = W.config(cid, seed, with_rows=False)
+    ro, rg, rows, cap, _, _ = _prep(wl)
+    if cid == 3:
+        counts = np.asarray(ro.tokens_per_expert)
+        assert int(np.sum(counts > wl.capacity)) == 2 and int(np.sum(counts == 0)) == 1
+    rng = np.random.default_rng(2000 + 10 * cid + seed)
+    x = W.normal(rng, (wl.T, 40), W.BF16)
+    xg = to_dev(x, W.BF16)
+    yg = peg.gather_binned(xg, rg) if wl.layout == W.BINNED else peg.gather_padded(xg, rg)
+    assert yg.shape[0] == oracle.expert_rows(ro, wl.layout, cap)
+    _check_gather_full(yg, xg, rows, wl.K, "narrow gather")
+    assert int(peg.validate_routing(rg, n_indices=ro.n).item()) == 0
