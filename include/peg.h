@@ -64,7 +64,10 @@ typedef int32_t peg_status;
 #define PEG_BINNED 0 /* [E, C, H]: row = e*C + offset, offsets >= C dropped ([BIN]) */
 #define PEG_PADDED 1 /* [padded_bins[E-1], H]: row = padded_start(e) + offset ([PAD]) */
 
-/* Limits enforced by the host checks. */
+/* Limits enforced by the host checks. Besides the limits each call lists,
+ * every call returns PEG_ERR_BAD_SHAPE when one of its launches would exceed
+ * 2^32 - 1 threads (a HIP dispatch counts its threads in 32 bits): for the
+ * row kernels this is T above about 16.7 million tokens. */
 #define PEG_MAX_EXPERTS 1024
 
 /* Bits of the flag word written by peg_validate_routing and of the

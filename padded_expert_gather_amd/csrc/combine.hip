@@ -428,6 +428,7 @@ static peg_status combine_dispatch(int vec, hipStream_t s, const uint8_t* y, uin
     const RowShape sh = combine_shape(K);
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
+    if (!grid_fits(token_blocks(T, sh.wpt), kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)token_blocks(T, sh.wpt));
     switch (vec) {
         case 16: return combine_vec<DT, 16>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
@@ -547,6 +548,7 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
     const int64_t tb = token_blocks(T, sh.wpt);
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)grad, wgrad, nch, q, T, K, slot_row, ra, E, nullptr,
                       nullptr, 0, layout, capacity, bins, tb};
+    if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
     return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
 }
 
@@ -573,6 +575,7 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
     const int64_t tb = token_blocks(T, sh.wpt);
+    if (!grid_fits(tb + gap_blocks(dy_rows, nch), kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)(tb + gap_blocks(dy_rows, nch)));
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)dout, wgrad, nch, q, T, K, slot_row, ra, E, weights,
                       (uint8_t*)dy, dy_rows, layout, capacity, bins, tb};

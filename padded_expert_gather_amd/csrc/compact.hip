@@ -82,6 +82,7 @@ PEG_API peg_status peg_routing_map_compact(const void* probs, int32_t probs_dtyp
     if (!aligned(probs, elem_bytes(probs_dtype)) || !aligned(probs_out, 4) || !aligned(route_experts, 4))
         return PEG_ERR_ALIGNMENT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!grid_fits((T + kRowsPerBlock - 1) / kRowsPerBlock, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
     if (probs_dtype == PEG_F32)
         return launch(compact_kernel<PEG_F32>, grid, dim3(kBlock), 0, s, probs, routing_map, T, E, topk, probs_out,
@@ -102,6 +103,7 @@ PEG_API peg_status peg_routing_map_compact_backward(const float* grad_probs_out,
     if (!aligned(grad_probs_out, 4) || !aligned(route_experts, 4) || !aligned(grad_probs, 4))
         return PEG_ERR_ALIGNMENT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!grid_fits((T + kRowsPerBlock - 1) / kRowsPerBlock, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
     return launch(compact_backward_kernel, grid, dim3(kBlock), 0, s, grad_probs_out, route_experts, T, E, topk,
                   grad_probs);

@@ -158,6 +158,7 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
     const int64_t nz = gap_blocks(out_rows, nch);
     const int wpt = gather_wpt(nch);
     const int64_t tb = token_blocks(T, wpt);
+    if (!grid_fits(tb + nz, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)(tb + nz));
     const int64_t slice = wave_slice(nch, wpt);
     const int u = lanes_per_pass(slice);
@@ -234,6 +235,7 @@ PEG_API peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int6
     // are never read
     const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, slice, K, slot_row, out_rows, PEG_BINNED, 1, 1,
                        nullptr, nullptr, T, tb, err_flag};
+    if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (wpt == 2) {

@@ -136,6 +136,12 @@ inline size_t ws_need(int64_t T, int32_t K, int32_t E) {
     return need < 256 ? 256 : need;
 }
 
+// A HIP dispatch holds its size in threads as a 32-bit number: a launch of
+// `blocks` blocks of `threads` threads must stay within it.
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+    return blocks >= 0 && blocks <= (int64_t)0xFFFFFFFF / threads;
+}
+
 // Launch through hipLaunchKernel so that the status of this very launch is
 // returned (no reliance on the thread's sticky last-error state).
 template <typename... KArgs, size_t... I>

@@ -273,10 +273,13 @@ struct GateArgs {
 
 template <int DT, int G, int CPL, int KS>
 static peg_status gate_launch(hipStream_t s, const GateArgs& a) {
-    if (a.ntiles > 0)
+    if (a.ntiles > 0) {
+        if (!grid_fits(a.ntiles, kHistThreads)) return PEG_ERR_BAD_SHAPE;
         return launch(router_hist_kernel<DT, G, CPL, KS>, dim3((unsigned)a.ntiles), dim3(kHistThreads), 0, s,
                       a.logits, a.T, a.E, a.K, a.gating, a.normalize, a.tile, a.ntiles, a.top, a.w, a.counts);
+    }
     constexpr int TPB = kBlock / G;
+    if (!grid_fits((a.T + TPB - 1) / TPB, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)((a.T + TPB - 1) / TPB));
     return launch(router_topk_kernel<DT, G, CPL, KS>, grid, dim3(kBlock), 0, s, a.logits, a.T, a.E, a.K, a.gating,
                   a.normalize, a.top, a.w);

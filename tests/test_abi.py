@@ -228,6 +228,28 @@ def test_compaction_and_validate_checks(lib):
     assert v(_p(FAKE), _p(FAKE), _p(FAKE), None, 4, 2, 4, -1, _p(FAKE), None, 0, None) == WORKSPACE
 
 
+def test_oversized_launches_refused(lib):
+    """A launch past 2^32 - 1 threads (a HIP dispatch counts threads in 32
+    bits) is refused with BAD_SHAPE before anything is enqueued."""
+    g = lib.peg_gather_rows
+    assert g(_p(FAKE), 1, 40_000_000, 8, 1, _p(FAKE), _p(FAKE), 16, None, None) == BAD_SHAPE
+    b = lib.peg_gather_binned
+    assert b(_p(FAKE), 1, 40_000_000, 8, 1, 4, 2, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 1 << 20,
+             None) == BAD_SHAPE
+    c = lib.peg_scatter_combine
+    assert c(_p(FAKE), 1, 0, 20_000_000, 8, 1, 4, 2, _p(FAKE), _p(FAKE), _p(FAKE), None, _p(FAKE), None, _p(FAKE),
+             _p(FAKE), 1 << 20, None) == BAD_SHAPE
+    w = lib.peg_wgrad
+    assert w(_p(FAKE), _p(FAKE), 1, 0, 80_000_000, 8, 2, 4, 2, _p(FAKE), _p(FAKE), _p(FAKE), None, _p(FAKE),
+             _p(FAKE), _p(FAKE), 1 << 20, None) == BAD_SHAPE
+    r = lib.peg_router_topk
+    assert r(_p(FAKE), 0, 1 << 29, 2, 1, 0, 1, _p(FAKE), _p(FAKE), None) == BAD_SHAPE
+    f = lib.peg_routing_map_compact
+    assert f(_p(FAKE), 0, _p(FAKE), (1 << 31) - 1, 1, 1, _p(FAKE), _p(FAKE), None) == BAD_SHAPE
+    fb = lib.peg_routing_map_compact_backward
+    assert fb(_p(FAKE), _p(FAKE), (1 << 31) - 1, 1, 1, _p(FAKE), None) == BAD_SHAPE
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

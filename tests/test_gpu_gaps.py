@@ -1,0 +1,111 @@
+"""GPU: zeroing of the gap rows of large expert tensors (hundreds of MB,
+mostly gap), against the oracle's gather, bit for bit.
+
+Every output buffer is filled with 0xFF bytes first, so a gap row that is
+not written shows up as a mismatch. Cases: 16-, 8-, 4- and 2-byte row
+vectors; binned with dropped routes and mostly empty capacity; padded with a
+large multiple; padded with a multiple of 2 and a buffer far longer than the
+padded rows, so that each gap block's range crosses the gaps of many
+experts (rows past padded_bins[E-1] must stay untouched); a buffer cut short
+of padded_bins[E-1]; E = 1 and E = 64; all routes absent.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import padded_expert_gather_amd as peg
+import workloads as W
+from gpu_util import DEV, bits_equal, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+LARGE_UNITS = 1 << 24  # row vectors of every tensor here
+ELEM = {W.F32: 4, W.BF16: 2, W.F16: 2}
+
+
+def _vec_units(H, dtype):
+    """Row vectors of the widest lane (16, 8, 4 or 2 bytes) dividing the row."""
+    rb = H * ELEM[dtype]
+    for v in (16, 8, 4, 2):
+        if rb % v == 0 and v >= ELEM[dtype]:
+            return rb // v
+    raise AssertionError
+
+
+W_TORCH = {W.F32: torch.float32, W.BF16: torch.bfloat16, W.F16: torch.float16}
+
+
+def _filled(rows, H, dtype):
+    t = torch.empty((rows, H), dtype=W_TORCH[dtype], device=DEV)
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+@pytest.mark.parametrize("T,K,E,H,dtype,C,none_frac,skew", [
+    (100000, 4, 64, 64, W.BF16, 32768, 0.0, 0.3),    # 16-byte vectors, 87% gap rows, drops
+    (60000, 2, 64, 12, W.BF16, 98304, 0.1, 0.0),     # 8-byte vectors
+    (80000, 2, 32, 7, W.F32, 262144, 0.0, 0.5),      # 4-byte vectors
+    (50000, 8, 64, 5, W.BF16, 65536, 0.0, 2.0),      # 2-byte vectors, heavy skew
+    (300000, 1, 1, 256, W.BF16, 524288, 0.2, 0.0),   # E = 1
+    (20000, 2, 64, 64, W.BF16, 32768, 1.0, 0.0),     # no route at all: every row is gap
+])
+def test_large_gaps_binned(T, K, E, H, dtype, C, none_frac, skew):
+    print(f"[gaps binned] T{T} K{K} E{E} H{H} C{C} dtype{dtype}", flush=True)
+    assert E * C * _vec_units(H, dtype) >= LARGE_UNITS
+    rng = np.random.default_rng(T + H)
+    top, _ = W.random_routing(rng, T, K, E, none_frac=none_frac, skew=skew)
+    x = W.normal(rng, (T, H), dtype)
+    ro = oracle.route_prep(top, E)
+    rg = peg.route_prep(to_dev(top), E, capacity=C)
+    out = _filled(E * C, H, dtype)
+    peg.gather_binned(to_dev(x, dtype), rg, out=out)
+    bits_equal(to_host(out), oracle.gather(x, ro, W.BINNED, C), "binned gather")
+    out.view(torch.uint8).fill_(0xFF)
+    peg.gather_binned(to_dev(x, dtype), rg, out=out, use_slot_row=False)
+    bits_equal(to_host(out), oracle.gather(x, ro, W.BINNED, C), "binned gather (rebuilt map)")
+
+
+@pytest.mark.parametrize("T,K,E,H,dtype,m,extra_rows", [
+    (200000, 2, 64, 5, W.BF16, 65536, 0),            # large multiple, 2-byte vectors
+    (3000, 2, 64, 1, W.F32, 2, (1 << 24) + 11),      # gaps of 0-1 rows: a block's range spans many experts
+    (5000, 4, 48, 64, W.BF16, 2, (1 << 21) + 5),     # same with 16-byte vectors
+])
+def test_large_gaps_padded(T, K, E, H, dtype, m, extra_rows):
+    print(f"[gaps padded] T{T} K{K} E{E} H{H} m{m} extra{extra_rows}", flush=True)
+    rng = np.random.default_rng(T + E)
+    top, _ = W.random_routing(rng, T, K, E, skew=0.2)
+    x = W.normal(rng, (T, H), dtype)
+    ro = oracle.route_prep(top, E, pad_multiple=m)
+    rg = peg.route_prep(to_dev(top), E, pad_multiple=m)
+    R = int(ro.padded_bins[-1])
+    rows = R + extra_rows
+    assert rows * _vec_units(H, dtype) >= LARGE_UNITS
+    out = _filled(rows, H, dtype)
+    peg.gather_padded(to_dev(x, dtype), rg, out=out)
+    host = to_host(out)
+    bits_equal(host[:R], oracle.gather(x, ro, W.PADDED), "padded gather")
+    assert (host[R:].view(np.uint8) == 0xFF).all(), "rows past padded_bins[E-1] were written"
+
+
+def test_large_gaps_cut_buffer():
+    """A buffer shorter than padded_bins[E-1]: the rows it holds match, the
+    flag is raised and nothing past the buffer is written."""
+    print("[gaps cut]", flush=True)
+    rng = np.random.default_rng(11)
+    T, K, E, H, m = 50000, 2, 64, 40, 65536
+    top, _ = W.random_routing(rng, T, K, E, skew=0.1)
+    x = W.normal(rng, (T, H), W.BF16)
+    ro = oracle.route_prep(top, E, pad_multiple=m)
+    rg = peg.route_prep(to_dev(top), E, pad_multiple=m)
+    R = int(ro.padded_bins[-1])
+    small = R - 3 * m - 17
+    assert small * _vec_units(H, W.BF16) >= LARGE_UNITS
+    buf = _filled(small + 100, H, W.BF16)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    peg.gather_padded(to_dev(x, W.BF16), rg, out=buf[:small], err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & peg.FLAG_OUT_ROWS
+    host = to_host(buf)
+    bits_equal(host[:small], oracle.gather(x, ro, W.PADDED)[:small], "cut padded gather")
+    assert (host[small:].view(np.uint8) == 0xFF).all(), "rows past the buffer were written"
