@@ -370,7 +370,20 @@ def cpu_baseline(wl, W, seconds, bytes_step):
     per_step = t_total / reps
     return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole step(s) of the same workload (seed 0), {per_step * 1e3:.1f} ms per step, "
-                      f"1 thread; tokens/s {wl.T / per_step:.1f}"}
+                      f"1 thread; tokens/s {wl.T / per_step:.1f}",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name, as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def traffic_for(kernel, workload_name):
@@ -478,7 +491,8 @@ def main():
             ms = [hip.elapsed_ms(evs[i][n][0], evs[i][n][1]) for i in range(args.steps)]
             avg = sum(ms) / len(ms)
             entry = {"avg_us": round(avg * 1e3, 2), "median_us": round(median(ms) * 1e3, 2),
-                     "min_us": round(min(ms) * 1e3, 2)}
+                     "min_us": round(min(ms) * 1e3, 2), "tokens_per_s": round(wl.T / (avg / 1e3), 1),
+                     "assignments_per_s": round(sz["n"] / (avg / 1e3), 1)}
             if n in ab:
                 entry["bytes"] = ab[n]
                 entry["GBps"] = round(ab[n] / (avg / 1e3) / 1e9, 1)

@@ -128,6 +128,26 @@ static peg_status gather_launch(int u, dim3 grid, hipStream_t s, const GatherArg
 #undef PEG_GATHER_U
 }
 
+template <int WPT>
+static peg_status gather_vec(int vec, int u, dim3 grid, hipStream_t s, const GatherArgs& a) {
+    switch (vec) {
+        case 16: return gather_launch<16, WPT>(u, grid, s, a);
+        case 8: return gather_launch<8, WPT>(u, grid, s, a);
+        case 4: return gather_launch<4, WPT>(u, grid, s, a);
+        default: return gather_launch<2, WPT>(u, grid, s, a);
+    }
+}
+
+// Waves per token 2, 4 and 8 are built; 16 only when PEG_GATHER_WPT asks for it.
+static peg_status gather_dispatch(int wpt, int vec, int u, dim3 grid, hipStream_t s, const GatherArgs& a) {
+    if (wpt == 2) return gather_vec<2>(vec, u, grid, s, a);
+    if (wpt == 8) return gather_vec<8>(vec, u, grid, s, a);
+#if PEG_GATHER_WPT == 16
+    if (wpt == 16) return gather_vec<16>(vec, u, grid, s, a);
+#endif
+    return gather_vec<4>(vec, u, grid, s, a);
+}
+
 static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t H, int32_t K, int32_t E,
                                 int32_t layout, int32_t capacity, const int32_t* indices, const int32_t* bin_ids,
                                 const int32_t* bins, const int32_t* padded_bins, const int32_t* slot_row,
@@ -156,7 +176,7 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
     }
     const int64_t nch = row_bytes / vec;
     const int64_t nz = gap_blocks(out_rows, nch);
-    const int wpt = gather_wpt(nch);
+    const int wpt = gather_wpt(nch, K);
     const int64_t tb = token_blocks(T, wpt);
     if (!grid_fits(tb + nz, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)(tb + nz));
@@ -164,30 +184,7 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
     const int u = lanes_per_pass(slice);
     const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, slice, K, slot_row, out_rows, layout, E, capacity,
                        bins, padded_bins, T, tb, err_flag};
-    if (wpt == 2) {
-        switch (vec) {
-            case 16: return gather_launch<16, 2>(u, grid, s, a);
-            case 8: return gather_launch<8, 2>(u, grid, s, a);
-            case 4: return gather_launch<4, 2>(u, grid, s, a);
-            default: return gather_launch<2, 2>(u, grid, s, a);
-        }
-    }
-#if PEG_GATHER_WPT > 4
-    if (wpt == PEG_GATHER_WPT) {
-        switch (vec) {
-            case 16: return gather_launch<16, PEG_GATHER_WPT>(u, grid, s, a);
-            case 8: return gather_launch<8, PEG_GATHER_WPT>(u, grid, s, a);
-            case 4: return gather_launch<4, PEG_GATHER_WPT>(u, grid, s, a);
-            default: return gather_launch<2, PEG_GATHER_WPT>(u, grid, s, a);
-        }
-    }
-#endif
-    switch (vec) {
-        case 16: return gather_launch<16, 4>(u, grid, s, a);
-        case 8: return gather_launch<8, 4>(u, grid, s, a);
-        case 4: return gather_launch<4, 4>(u, grid, s, a);
-        default: return gather_launch<2, 4>(u, grid, s, a);
-    }
+    return gather_dispatch(wpt, vec, u, grid, s, a);
 }
 
 }  // namespace peg
@@ -227,7 +224,7 @@ PEG_API peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int6
     if (vec == 0) return PEG_ERR_ALIGNMENT;
     if (T == 0) return PEG_OK;
     const int64_t nch = row_bytes / vec;
-    const int wpt = gather_wpt(nch);
+    const int wpt = gather_wpt(nch, K);
     const int64_t tb = token_blocks(T, wpt);
     const int64_t slice = wave_slice(nch, wpt);
     const int u = lanes_per_pass(slice);
@@ -238,29 +235,6 @@ PEG_API peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int6
     if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (wpt == 2) {
-        switch (vec) {
-            case 16: return gather_launch<16, 2>(u, grid, s, a);
-            case 8: return gather_launch<8, 2>(u, grid, s, a);
-            case 4: return gather_launch<4, 2>(u, grid, s, a);
-            default: return gather_launch<2, 2>(u, grid, s, a);
-        }
-    }
-#if PEG_GATHER_WPT > 4
-    if (wpt == PEG_GATHER_WPT) {
-        switch (vec) {
-            case 16: return gather_launch<16, PEG_GATHER_WPT>(u, grid, s, a);
-            case 8: return gather_launch<8, PEG_GATHER_WPT>(u, grid, s, a);
-            case 4: return gather_launch<4, PEG_GATHER_WPT>(u, grid, s, a);
-            default: return gather_launch<2, PEG_GATHER_WPT>(u, grid, s, a);
-        }
-    }
-#endif
-    switch (vec) {
-        case 16: return gather_launch<16, 4>(u, grid, s, a);
-        case 8: return gather_launch<8, 4>(u, grid, s, a);
-        case 4: return gather_launch<4, 4>(u, grid, s, a);
-        default: return gather_launch<2, 4>(u, grid, s, a);
-    }
+    return gather_dispatch(wpt, vec, u, grid, s, a);
 }
 

@@ -35,11 +35,11 @@ inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, con
     return 0;
 }
 
-// The token kernels give each token WPT waves (4, 2 or 1) of a 4-wave
-// block, so a block holds 4 / WPT tokens. Measured on MI355X: the gather
-// likes 2 waves per token for rows of at most 512 vectors and 4 above, the
-// combine 4, wgrad and the combine backward 2 (1 when K <= 2; the per-K
-// values sit with those kernels).
+// The token kernels give each token WPT waves of a 4-wave block, so a block
+// holds 4 / WPT tokens (WPT 8 or 16: a token spans 2 or 4 blocks). Measured
+// on MI355X: the gather's choice is below; the combine likes 4, wgrad and
+// the combine backward 2 (1 when K <= 2; the per-K values sit with those
+// kernels).
 #ifndef PEG_COMBINE_WPT
 #define PEG_COMBINE_WPT 4
 #endif
@@ -51,15 +51,19 @@ inline int pick_vec(int64_t row_bytes, int eb, const void* a, const void* b, con
 #endif
 
 // Waves per token of the gather: 2 up to PEG_GATHER_WPT_SPLIT vectors per
-// row, else 4; PEG_GATHER_WPT (8 or 16) overrides it, a token then spanning
-// 2 or 4 blocks. Measured: 8 or 16 waves win 3% on some rows (768 or 896
-// vectors) and lose 5-25% on others (448 and 512), so the default stays.
+// row; above it 8 (a token over 2 blocks) when K <= 2, else 4. Measured
+// (gather alone, bf16, HIP events, 3 runs of 40 launches): T4096 H4096 K2
+// 19.6 us at 2 against 21.7 at 4 and 24.3 at 8; T16384 H6144 K2 126.7 us at
+// 4 against 121.9 at 8; T8192 H7168 E256 K8 161-162 us at 4 against 164 at
+// 8; T32768 H3584 K8 395 us at 2, 391 at 4, 416 at 8. PEG_GATHER_WPT (2, 4,
+// 8 or 16) overrides the rule.
 #ifndef PEG_GATHER_WPT
 #define PEG_GATHER_WPT 0
 #endif
-inline int gather_wpt(int64_t nch) {
+inline int gather_wpt(int64_t nch, int32_t K) {
     if (PEG_GATHER_WPT > 0) return PEG_GATHER_WPT;
-    return nch <= PEG_GATHER_WPT_SPLIT ? 2 : 4;
+    if (nch <= PEG_GATHER_WPT_SPLIT) return 2;
+    return K <= 2 ? 8 : 4;
 }
 
 template <int WPT>
