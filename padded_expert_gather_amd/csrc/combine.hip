@@ -361,6 +361,16 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
 #ifndef PEG_COMBINE_UMAX_K2
 #define PEG_COMBINE_UMAX_K2 PEG_COMBINE_UMAX
 #endif
+// K > 2 with rows of at most PEG_COMBINE_SPLIT vectors: PEG_COMBINE_WPT_SHORT
+// waves per token, so that a wave still covers about 256 vectors in one pass
+// (T32768 H3584 K8: 144.5 us at 2 waves against 150.4 at 4; T8192 H7168
+// K8 keeps 4: 104.9 us against 110.9 at 2).
+#ifndef PEG_COMBINE_SPLIT
+#define PEG_COMBINE_SPLIT 512
+#endif
+#ifndef PEG_COMBINE_WPT_SHORT
+#define PEG_COMBINE_WPT_SHORT 2
+#endif
 #ifndef PEG_WGRAD_UMAX
 #define PEG_WGRAD_UMAX 2
 #endif
@@ -374,11 +384,23 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
 struct RowShape {
     int wpt, umax;
 };
-static RowShape combine_shape(int32_t K) {
-    return K <= 2 ? RowShape{PEG_COMBINE_WPT_K2, PEG_COMBINE_UMAX_K2} : RowShape{PEG_COMBINE_WPT, PEG_COMBINE_UMAX};
+static RowShape combine_shape(int32_t K, int64_t nch) {
+    if (K <= 2) return RowShape{PEG_COMBINE_WPT_K2, PEG_COMBINE_UMAX_K2};
+    return RowShape{nch <= PEG_COMBINE_SPLIT ? PEG_COMBINE_WPT_SHORT : PEG_COMBINE_WPT, PEG_COMBINE_UMAX};
 }
-static RowShape wgrad_shape(int32_t K) {
-    return K <= 2 ? RowShape{PEG_WGRAD_WPT_K2, PEG_WGRAD_UMAX_K2} : RowShape{PEG_WGRAD_WPT, PEG_WGRAD_UMAX};
+// K > 2 with rows above PEG_WGRAD_SPLIT vectors: PEG_WGRAD_WPT_LONG waves
+// per token (T8192 H7168 K8: wgrad 90.5 us at 4 waves against 94.9 at 2,
+// the combine backward 271.6 against 283.7; T32768 H3584 K8 keeps 2: wgrad
+// 121.5 us against 131.5 at 4).
+#ifndef PEG_WGRAD_SPLIT
+#define PEG_WGRAD_SPLIT 512
+#endif
+#ifndef PEG_WGRAD_WPT_LONG
+#define PEG_WGRAD_WPT_LONG 4
+#endif
+static RowShape wgrad_shape(int32_t K, int64_t nch) {
+    if (K <= 2) return RowShape{PEG_WGRAD_WPT_K2, PEG_WGRAD_UMAX_K2};
+    return RowShape{nch > PEG_WGRAD_SPLIT ? PEG_WGRAD_WPT_LONG : PEG_WGRAD_WPT, PEG_WGRAD_UMAX};
 }
 #ifndef PEG_BACKWARD_WPT_K2
 #define PEG_BACKWARD_WPT_K2 PEG_WGRAD_WPT_K2
@@ -392,8 +414,12 @@ static RowShape wgrad_shape(int32_t K) {
 #ifndef PEG_BACKWARD_UMAX
 #define PEG_BACKWARD_UMAX PEG_WGRAD_UMAX
 #endif
-static RowShape backward_shape(int32_t K) {
-    return K <= 2 ? RowShape{PEG_BACKWARD_WPT_K2, PEG_BACKWARD_UMAX_K2} : RowShape{PEG_BACKWARD_WPT, PEG_BACKWARD_UMAX};
+#ifndef PEG_BACKWARD_WPT_LONG
+#define PEG_BACKWARD_WPT_LONG PEG_WGRAD_WPT_LONG
+#endif
+static RowShape backward_shape(int32_t K, int64_t nch) {
+    if (K <= 2) return RowShape{PEG_BACKWARD_WPT_K2, PEG_BACKWARD_UMAX_K2};
+    return RowShape{nch > PEG_WGRAD_SPLIT ? PEG_BACKWARD_WPT_LONG : PEG_BACKWARD_WPT, PEG_BACKWARD_UMAX};
 }
 
 // Vectors per lane per pass: 1, 2 or 4, capped.
@@ -403,40 +429,45 @@ static int pass_vectors(int64_t slice, int cap) {
 }
 
 template <int DT, int VEC, int U>
-static peg_status combine_go(dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch, int64_t q,
-                             int64_t T, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
+static peg_status combine_go(int wpt, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
+                             int64_t q, int64_t T, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra,
+                             int32_t E) {
 #define PEG_COMBINE_LAUNCH(WPT, KR)                                                                            \
     return launch(combine_kernel<DT, VEC, U, WPT, KR>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K, slot_row, \
                   w, ra.static_rows, ra.padded_bins, E)
     if (K <= 2) PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT_K2, 2);
+#if PEG_COMBINE_WPT_SHORT != PEG_COMBINE_WPT
+    if (wpt == PEG_COMBINE_WPT_SHORT) PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT_SHORT, kRowsFast);
+#endif
+    (void)wpt;
     PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT, kRowsFast);
 #undef PEG_COMBINE_LAUNCH
 }
 
 template <int DT, int VEC>
-static peg_status combine_vec(int u, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch,
-                              int64_t q, int64_t T, int32_t K, const int32_t* slot_row, const float* w, RowArgs ra,
-                              int32_t E) {
-    if (u == 1) return combine_go<DT, VEC, 1>(grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
-    if (u == 2) return combine_go<DT, VEC, 2>(grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
-    return combine_go<DT, VEC, 4>(grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+static peg_status combine_vec(int wpt, int u, dim3 grid, hipStream_t s, const uint8_t* y, uint8_t* out,
+                              int64_t nch, int64_t q, int64_t T, int32_t K, const int32_t* slot_row, const float* w,
+                              RowArgs ra, int32_t E) {
+    if (u == 1) return combine_go<DT, VEC, 1>(wpt, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+    if (u == 2) return combine_go<DT, VEC, 2>(wpt, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+    return combine_go<DT, VEC, 4>(wpt, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
 }
 
 template <int DT>
 static peg_status combine_dispatch(int vec, hipStream_t s, const uint8_t* y, uint8_t* out, int64_t nch, int64_t T,
                                    int32_t K, const int32_t* slot_row, const float* w, RowArgs ra, int32_t E) {
-    const RowShape sh = combine_shape(K);
+    const RowShape sh = combine_shape(K, nch);
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
     if (!grid_fits(token_blocks(T, sh.wpt), kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)token_blocks(T, sh.wpt));
     switch (vec) {
-        case 16: return combine_vec<DT, 16>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
-        case 8: return combine_vec<DT, 8>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
-        case 4: return combine_vec<DT, 4>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+        case 16: return combine_vec<DT, 16>(sh.wpt, u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+        case 8: return combine_vec<DT, 8>(sh.wpt, u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+        case 4: return combine_vec<DT, 4>(sh.wpt, u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
         default:
             if constexpr (Elem<DT>::bytes == 2)
-                return combine_vec<DT, 2>(u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
+                return combine_vec<DT, 2>(sh.wpt, u, grid, s, y, out, nch, q, T, K, slot_row, w, ra, E);
             return PEG_ERR_ALIGNMENT;
     }
 }
@@ -457,6 +488,7 @@ struct WgradArgs {
     int32_t layout, capacity;
     const int32_t* bins;
     int64_t token_blocks;
+    int wpt;  // waves per token of the launch
 };
 
 template <int DT, int VEC, int U, int DY>
@@ -469,8 +501,18 @@ static peg_status wgrad_go(dim3 grid, hipStream_t s, const WgradArgs& a) {
         if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, 2>));
         else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT_K2, DY, 2>));
     }
-    if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT, kRowsFast>));
-    else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT, DY, kRowsFast>));
+    if constexpr (DY == 0) {
+#if PEG_WGRAD_WPT_LONG != PEG_WGRAD_WPT
+        if (a.wpt == PEG_WGRAD_WPT_LONG) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_LONG, kRowsFast>));
+#endif
+        PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT, kRowsFast>));
+    } else {
+#if PEG_BACKWARD_WPT_LONG != PEG_BACKWARD_WPT
+        if (a.wpt == PEG_BACKWARD_WPT_LONG)
+            PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT_LONG, DY, kRowsFast>));
+#endif
+        PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT, DY, kRowsFast>));
+    }
 #undef PEG_WGRAD_LAUNCH
 }
 
@@ -542,12 +584,12 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const RowShape sh = wgrad_shape(K);
+    const RowShape sh = wgrad_shape(K, nch);
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
     const int64_t tb = token_blocks(T, sh.wpt);
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)grad, wgrad, nch, q, T, K, slot_row, ra, E, nullptr,
-                      nullptr, 0, layout, capacity, bins, tb};
+                      nullptr, 0, layout, capacity, bins, tb, sh.wpt};
     if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
     return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
 }
@@ -571,14 +613,14 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;
-    const RowShape sh = backward_shape(K);
+    const RowShape sh = backward_shape(K, nch);
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
     const int64_t tb = token_blocks(T, sh.wpt);
     if (!grid_fits(tb + gap_blocks(dy_rows, nch), kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)(tb + gap_blocks(dy_rows, nch)));
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)dout, wgrad, nch, q, T, K, slot_row, ra, E, weights,
-                      (uint8_t*)dy, dy_rows, layout, capacity, bins, tb};
+                      (uint8_t*)dy, dy_rows, layout, capacity, bins, tb, sh.wpt};
     if (weights) return wgrad_by_dtype<2>(dtype, vec, u, grid, s, a);
     return wgrad_by_dtype<1>(dtype, vec, u, grid, s, a);
 }

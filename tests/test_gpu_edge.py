@@ -84,6 +84,8 @@ CASES = [
     _case("K16_padded_f32", 200, 16, 32, 40, W.F32, P, m=8, none_frac=0.2),
     _case("K9_f16", 150, 9, 12, 24, W.F16, B, cap=90),
     _case("H16384_bf16", 64, 2, 4, 16384, W.BF16, P, m=16),
+    _case("K4_long_rows", 300, 4, 16, 4100, W.BF16, B, cap=100, skew=0.1),
+    _case("K3_long_rows_f32", 200, 3, 8, 1030, W.F32, P, m=8, none_frac=0.1),
     _case("T0_binned", 0, 2, 4, 32, W.BF16, B, cap=4),
     _case("T0_padded", 0, 2, 4, 32, W.BF16, P, m=4),
 ]
