@@ -45,6 +45,8 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
+        if os.environ.get("PEG_LIBRARY"):
+            raise OSError(f"PEG_LIBRARY names {LIB_PATH}, which does not exist")
         from . import build as _build
         _build.build()
     lib = ctypes.CDLL(LIB_PATH)
@@ -270,11 +272,30 @@ def _slot(r, use_slot_row):
     return r.slot_row if use_slot_row else None
 
 
+def _same_device(r, t, name):
+    if r.bins.device != t.device:
+        raise ValueError(f"{name} is on {t.device}, the routing on {r.bins.device}")
+
+
+def _expert_tensor(y, r, name):
+    """y must be a 2-D expert tensor on the routing's device; a binned layout
+    needs at least E*C rows (a padded one padded_bins[E-1] rows, which the
+    caller guarantees: checking it would synchronise)."""
+    if y.dim() != 2:
+        raise ValueError(f"{name} must be [rows, H]")
+    _same_device(r, y, name)
+    if r.layout == BINNED and r.capacity is not None and y.shape[0] < r.E * r.capacity:
+        raise ValueError(f"{name} must have E*C = {r.E * r.capacity} rows, got {y.shape[0]}")
+
+
 def gather_binned(x, r, out=None, ws=None, use_slot_row=True):
     """Binned dispatch: [E*C, H] with every row written (zeros for unused capacity)."""
     x = _dev(x, "x")
     if r.layout != BINNED and r.capacity is None:
         raise ValueError("routing has no capacity")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
+    _same_device(r, x, "x")
     T, H = x.shape
     if T != r.T:
         raise ValueError("x rows != T")
@@ -299,6 +320,9 @@ def gather_padded(x, r, out=None, out_rows=None, err_flag=None, ws=None, use_slo
     x = _dev(x, "x")
     if r.padded_bins is None:
         raise ValueError("routing has no padded_bins")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
+    _same_device(r, x, "x")
     T, H = x.shape
     if T != r.T:
         raise ValueError("x rows != T")
@@ -321,6 +345,7 @@ def gather_padded(x, r, out=None, out_rows=None, err_flag=None, ws=None, use_slo
 def scatter_combine(y, r, weights=None, out=None, ws=None, use_slot_row=True):
     """out[t] = sum over kept k of w[t, k] * y[row(t, k)] (fp32 accumulate), [T, H] in y's dtype."""
     y = _dev(y, "y")
+    _expert_tensor(y, r, "y")
     H = y.shape[1]
     if weights is not None:
         weights = _dev(weights, "weights", torch.float32)
@@ -344,6 +369,7 @@ def scatter_combine(y, r, weights=None, out=None, ws=None, use_slot_row=True):
 def wgrad(y, grad, r, out=None, ws=None, use_slot_row=True):
     """Router-weight gradient: [T, K] float32, <y[row(t,k)], grad[t]> for kept routes, else 0."""
     y = _dev(y, "y")
+    _expert_tensor(y, r, "y")
     grad = _dev(grad, "grad", y.dtype)
     H = y.shape[1]
     if grad.shape != (r.T, H):
@@ -351,6 +377,8 @@ def wgrad(y, grad, r, out=None, ws=None, use_slot_row=True):
     if out is None:
         out = torch.empty((r.T, r.K), dtype=torch.float32, device=y.device)
     _dev(out, "out", torch.float32)
+    if out.numel() != r.T * r.K:
+        raise ValueError("out must hold T*K values")
     ws, wsb = _ws(r.T, r.K, r.E, y.device, ws)
     with torch.cuda.device(y.device):
         st = _load().peg_wgrad(_ptr(y), _ptr(grad), _dtype_code(y, "y"), r.layout, r.T, H, r.K, r.E,
@@ -366,6 +394,7 @@ def combine_backward(y, dout, r, weights=None, dy=None, dy_rows=None, wgrad_out=
     dy[row(a)] = w[a] * dout[t] in the expert layout (gap rows zero; a raw copy
     when weights is None) and wgrad [T, K] f32 = <y[row(a)], dout[t]>."""
     y = _dev(y, "y")
+    _expert_tensor(y, r, "y")
     dout = _dev(dout, "dout", y.dtype)
     H = y.shape[1]
     if dout.shape != (r.T, H):
@@ -378,9 +407,13 @@ def combine_backward(y, dout, r, weights=None, dy=None, dy_rows=None, wgrad_out=
         rows = dy_rows if dy_rows is not None else (r.E * r.capacity if r.layout == BINNED else r.expert_rows())
         dy = torch.empty((rows, H), dtype=y.dtype, device=y.device)
     _dev(dy, "dy", y.dtype)
+    if dy.dim() != 2 or dy.shape[1] != H:
+        raise ValueError("dy must be [rows, H]")
     if wgrad_out is None:
         wgrad_out = torch.empty((r.T, r.K), dtype=torch.float32, device=y.device)
     _dev(wgrad_out, "wgrad_out", torch.float32)
+    if wgrad_out.numel() != r.T * r.K:
+        raise ValueError("wgrad_out must hold T*K values")
     ws, wsb = _ws(r.T, r.K, r.E, y.device, ws)
     with torch.cuda.device(y.device):
         st = _load().peg_combine_backward(_ptr(y), _ptr(dout), _ptr(weights), _dtype_code(y, "y"), r.layout, r.T, H,
@@ -433,6 +466,8 @@ def routing_map_compact(probs, routing_map, topk, probs_out=None, route_experts=
         route_experts = torch.empty((T, topk), dtype=torch.int32, device=probs.device)
     _dev(probs_out, "probs_out", torch.float32)
     _dev(route_experts, "route_experts", torch.int32)
+    if probs_out.numel() != T * topk or route_experts.numel() != T * topk:
+        raise ValueError("probs_out and route_experts must hold T*topk values")
     with torch.cuda.device(probs.device):
         st = _load().peg_routing_map_compact(_ptr(probs), _dtype_code(probs, "probs"), _ptr(rmap), T, E, int(topk),
                                              _ptr(probs_out), _ptr(route_experts), _stream(probs.device))
@@ -444,10 +479,16 @@ def routing_map_compact_backward(grad_probs_out, route_experts, num_experts, out
     """Scatter compact router gradients back to a dense [T, E] float32 tensor."""
     g = _dev(grad_probs_out, "grad_probs_out", torch.float32)
     idx = _dev(route_experts, "route_experts", torch.int32)
+    if idx.dim() != 2:
+        raise ValueError("route_experts must be [T, topk]")
     T, topk = idx.shape
+    if g.numel() != T * topk:
+        raise ValueError("grad_probs_out must match route_experts")
     if out is None:
         out = torch.empty((T, num_experts), dtype=torch.float32, device=g.device)
     _dev(out, "out", torch.float32)
+    if out.numel() != T * int(num_experts):
+        raise ValueError("out must be [T, num_experts]")
     with torch.cuda.device(g.device):
         st = _load().peg_routing_map_compact_backward(_ptr(g), _ptr(idx), T, int(num_experts), topk, _ptr(out),
                                                       _stream(g.device))
@@ -462,6 +503,12 @@ def validate_routing(r, n_indices=-1, indices=None, bin_ids=None, bins=None, pad
     bin_ids = r.bin_ids if bin_ids is None else bin_ids
     bins = r.bins if bins is None else bins
     padded_bins = r.padded_bins if padded_bins is None else padded_bins
+    for name, t, n in (("indices", indices, r.T * r.K), ("bin_ids", bin_ids, r.T * r.K), ("bins", bins, r.E),
+                       ("padded_bins", padded_bins, r.E)):
+        if t is not None:
+            _dev(t, name, torch.int32)
+            if t.numel() != n:
+                raise ValueError(f"{name} must hold {n} values")
     dev = bins.device
     flags = torch.empty(1, dtype=torch.int32, device=dev)
     ws, wsb = _ws(r.T, r.K, r.E, dev, ws)

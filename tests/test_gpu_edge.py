@@ -293,3 +293,37 @@ def test_compaction(E, topk, pdt):
     do = oracle.routing_map_compact_backward(g, io, E)
     dg = peg.routing_map_compact_backward(to_dev(g), ig, E)
     bits_equal(to_host(dg), do, "compaction backward")
+
+
+def test_binding_refuses_bad_buffers():
+    """The binding checks every buffer it can check without a sync before
+    anything is enqueued: output sizes, expert-tensor rows of the binned
+    layout, dy's row length, devices."""
+    rng = np.random.default_rng(8)
+    T, K, E, H, C = 64, 2, 4, 32, 40
+    top, w = W.random_routing(rng, T, K, E)
+    rg = peg.route_prep(to_dev(top), E, capacity=C)
+    xg = to_dev(W.normal(rng, (T, H), W.BF16), W.BF16)
+    y = peg.gather_binned(xg, rg)
+    with pytest.raises(ValueError):
+        peg.scatter_combine(y[: E * C - 1], rg)                       # fewer than E*C rows
+    with pytest.raises(ValueError):
+        peg.wgrad(y, xg, rg, out=torch.empty(T * K - 1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        peg.combine_backward(y, xg, rg, dy=torch.empty((E * C, H + 8), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        peg.combine_backward(y, xg, rg, wgrad_out=torch.empty(3, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        peg.gather_binned(xg.reshape(-1), rg)                         # x not [T, H]
+    probs = torch.rand((T, E), dtype=torch.float32, device=DEV)
+    rmap = torch.ones((T, E), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        peg.routing_map_compact(probs, rmap, 2, probs_out=torch.empty((T, 1), dtype=torch.float32, device=DEV))
+    idx = torch.zeros((T, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        peg.routing_map_compact_backward(torch.zeros((T, 2), device=DEV), idx, E,
+                                         out=torch.empty((T, E - 1), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        peg.validate_routing(rg, indices=rg.indices[:-1])
+    torch.cuda.synchronize()
+    assert int(peg.validate_routing(rg).item()) == 0                   # the routing itself is intact
