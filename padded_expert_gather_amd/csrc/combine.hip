@@ -398,9 +398,16 @@ static RowShape combine_shape(int32_t K, int64_t nch) {
 #ifndef PEG_WGRAD_WPT_LONG
 #define PEG_WGRAD_WPT_LONG 4
 #endif
+// The same for K <= 2: 2 waves instead of 1 above PEG_WGRAD_SPLIT vectors
+// (T16384 H6144 K2: wgrad 66.5 us against 67.5, the combine backward 177.1
+// against 181.6; T4096 H4096 keeps 1: backward 35.2 us against 37.3).
+#ifndef PEG_WGRAD_WPT_K2_LONG
+#define PEG_WGRAD_WPT_K2_LONG 2
+#endif
 static RowShape wgrad_shape(int32_t K, int64_t nch) {
-    if (K <= 2) return RowShape{PEG_WGRAD_WPT_K2, PEG_WGRAD_UMAX_K2};
-    return RowShape{nch > PEG_WGRAD_SPLIT ? PEG_WGRAD_WPT_LONG : PEG_WGRAD_WPT, PEG_WGRAD_UMAX};
+    const bool long_rows = nch > PEG_WGRAD_SPLIT;
+    if (K <= 2) return RowShape{long_rows ? PEG_WGRAD_WPT_K2_LONG : PEG_WGRAD_WPT_K2, PEG_WGRAD_UMAX_K2};
+    return RowShape{long_rows ? PEG_WGRAD_WPT_LONG : PEG_WGRAD_WPT, PEG_WGRAD_UMAX};
 }
 #ifndef PEG_BACKWARD_WPT_K2
 #define PEG_BACKWARD_WPT_K2 PEG_WGRAD_WPT_K2
@@ -417,9 +424,13 @@ static RowShape wgrad_shape(int32_t K, int64_t nch) {
 #ifndef PEG_BACKWARD_WPT_LONG
 #define PEG_BACKWARD_WPT_LONG PEG_WGRAD_WPT_LONG
 #endif
+#ifndef PEG_BACKWARD_WPT_K2_LONG
+#define PEG_BACKWARD_WPT_K2_LONG PEG_WGRAD_WPT_K2_LONG
+#endif
 static RowShape backward_shape(int32_t K, int64_t nch) {
-    if (K <= 2) return RowShape{PEG_BACKWARD_WPT_K2, PEG_BACKWARD_UMAX_K2};
-    return RowShape{nch > PEG_WGRAD_SPLIT ? PEG_BACKWARD_WPT_LONG : PEG_BACKWARD_WPT, PEG_BACKWARD_UMAX};
+    const bool long_rows = nch > PEG_WGRAD_SPLIT;
+    if (K <= 2) return RowShape{long_rows ? PEG_BACKWARD_WPT_K2_LONG : PEG_BACKWARD_WPT_K2, PEG_BACKWARD_UMAX_K2};
+    return RowShape{long_rows ? PEG_BACKWARD_WPT_LONG : PEG_BACKWARD_WPT, PEG_BACKWARD_UMAX};
 }
 
 // Vectors per lane per pass: 1, 2 or 4, capped.
@@ -498,8 +509,18 @@ static peg_status wgrad_go(dim3 grid, hipStream_t s, const WgradArgs& a) {
                   a.ra.static_rows, a.ra.padded_bins, a.E, a.weights, a.dy, a.dy_rows, a.layout, a.capacity, a.bins, \
                   a.token_blocks)
     if (a.K <= 2) {
-        if constexpr (DY == 0) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, 2>));
-        else PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT_K2, DY, 2>));
+        if constexpr (DY == 0) {
+#if PEG_WGRAD_WPT_K2_LONG != PEG_WGRAD_WPT_K2
+            if (a.wpt == PEG_WGRAD_WPT_K2_LONG) PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2_LONG, 2>));
+#endif
+            PEG_WGRAD_LAUNCH((wgrad_kernel<DT, VEC, U, PEG_WGRAD_WPT_K2, 2>));
+        } else {
+#if PEG_BACKWARD_WPT_K2_LONG != PEG_BACKWARD_WPT_K2
+            if (a.wpt == PEG_BACKWARD_WPT_K2_LONG)
+                PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT_K2_LONG, DY, 2>));
+#endif
+            PEG_WGRAD_LAUNCH((combine_backward_kernel<DT, VEC, U, PEG_BACKWARD_WPT_K2, DY, 2>));
+        }
     }
     if constexpr (DY == 0) {
 #if PEG_WGRAD_WPT_LONG != PEG_WGRAD_WPT
