@@ -7,7 +7,11 @@ preallocated buffers is captured once, then replayed three times with new
 inputs written into the captured input buffers between replays (eager work
 and synchronisations in between); every replay is compared with the eager
 results on the same inputs: index outputs and gathers bit for bit, floating
-outputs bit for bit too (same kernels, same launch shapes).
+outputs bit for bit too (same kernels, same launch shapes). A second graph
+holds the other entry points (router gating alone and fused with
+route_prep, compaction and its backward, the validator, the binned gather,
+combine and wgrad rebuilding the row map, row windows and the gather by row
+map) and is checked the same way.
 """
 import numpy as np
 import pytest
@@ -105,3 +109,106 @@ def test_graph_replays_match_eager():
                 g, e = g[:n_rows], e[:n_rows]
             assert torch.equal(g.view(torch.int16) if g.dtype == torch.bfloat16 else g,
                                e.view(torch.int16) if e.dtype == torch.bfloat16 else e), (seed, i)
+
+
+# ---------------------------------------------------------------------------
+# The other entry points in one captured graph: router gating (alone and
+# fused with route_prep), routing-map compaction and its backward, row
+# windows with the gather by row map, the validator, and the binned gather,
+# combine and wgrad rebuilding the row map from the sorted arrays.
+# ---------------------------------------------------------------------------
+E2, K2, TOPK, C2 = 16, 2, 4, 160
+
+
+def _inputs2(seed):
+    rng = np.random.default_rng(100 + seed)
+    logits = rng.standard_normal((T, E2), dtype=np.float32)
+    probs = rng.random((T, E2), dtype=np.float32)
+    rmap = (rng.random((T, E2)) < 0.2).astype(np.uint8)
+    gco = rng.standard_normal((T, TOPK), dtype=np.float32)
+    x = W.normal(rng, (T, H), W.BF16)
+    grad = W.normal(rng, (T, H), W.BF16)
+    base = (np.arange(E2) * C2 + rng.integers(0, 20, size=E2)).astype(np.int32)
+    limit = (np.arange(E2) * C2 + C2).astype(np.int32)
+    return logits, probs, rmap, gco, x, grad, base, limit
+
+
+def _buffers2():
+    i32 = dict(dtype=torch.int32, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    b = {"top": torch.empty((T, K2), **i32), "w": torch.empty((T, K2), **f32),
+         "top2": torch.empty((T, K2), **i32), "w2": torch.empty((T, K2), **f32),
+         "po": torch.empty((T, TOPK), **f32), "re": torch.empty((T, TOPK), **i32),
+         "gp": torch.empty((T, E2), **f32),
+         "flags": torch.empty(1, **i32), "y": torch.empty((E2 * C2, H), dtype=torch.bfloat16, device=DEV),
+         "yw": torch.empty((E2 * C2, H), dtype=torch.bfloat16, device=DEV),
+         "comb": torch.empty((T, H), dtype=torch.bfloat16, device=DEV), "wg": torch.empty((T, K2), **f32),
+         "ws": torch.empty(peg.workspace_bytes(T, K2, E2), dtype=torch.uint8, device=DEV)}
+    for name in ("idx", "bid", "slot", "idx_w", "bid_w", "slot_w"):
+        b[name] = torch.empty(T * K2, **i32)
+    for name in ("tpe", "bins", "tpe_w", "bins_w"):
+        b[name] = torch.empty(E2, **i32)
+    return b
+
+
+def _step2(inp, b):
+    logits, probs, rmap, gco, x, grad, base, limit = inp
+    lib = peg.library()
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: None if t is None else t.data_ptr()
+    ws, wsb = P(b["ws"]), b["ws"].numel()
+    assert lib.peg_router_topk(P(logits), peg.F32, T, E2, K2, peg.SOFTMAX, 1, P(b["top"]), P(b["w"]), st) == 0
+    assert lib.peg_route_prep_logits(P(logits), peg.F32, T, E2, K2, peg.SIGMOID, 0, peg.BINNED, C2, 0, P(b["top2"]),
+                                     P(b["w2"]), P(b["idx"]), P(b["bid"]), P(b["tpe"]), P(b["bins"]), None,
+                                     P(b["slot"]), ws, wsb, st) == 0
+    assert lib.peg_routing_map_compact(P(probs), peg.F32, P(rmap), T, E2, TOPK, P(b["po"]), P(b["re"]), st) == 0
+    assert lib.peg_routing_map_compact_backward(P(gco), P(b["re"]), T, E2, TOPK, P(b["gp"]), st) == 0
+    assert lib.peg_validate_routing(P(b["idx"]), P(b["bid"]), P(b["bins"]), None, T, K2, E2, -1, P(b["flags"]), ws,
+                                    wsb, st) == 0
+    # binned gather / combine / wgrad with the row map rebuilt from the sorted arrays
+    assert lib.peg_gather_binned(P(x), peg.BF16, T, H, K2, E2, C2, P(b["idx"]), P(b["bid"]), P(b["bins"]), None,
+                                 P(b["y"]), ws, wsb, st) == 0
+    assert lib.peg_scatter_combine(P(b["y"]), peg.BF16, peg.BINNED, T, H, K2, E2, C2, P(b["idx"]), P(b["bid"]),
+                                   P(b["bins"]), None, None, P(b["w2"]), P(b["comb"]), ws, wsb, st) == 0
+    assert lib.peg_wgrad(P(b["y"]), P(grad), peg.BF16, peg.BINNED, T, H, K2, E2, C2, P(b["idx"]), P(b["bid"]),
+                         P(b["bins"]), None, None, P(b["wg"]), ws, wsb, st) == 0
+    # row windows of the router's routes, then the gather by row map into a zeroed tensor
+    assert lib.peg_route_prep_windows(P(b["top"]), T, K2, E2, P(base), P(limit), P(b["idx_w"]), P(b["bid_w"]),
+                                      P(b["tpe_w"]), P(b["bins_w"]), P(b["slot_w"]), ws, wsb, st) == 0
+    b["yw"].zero_()  # a fill kernel, not a memset
+    assert lib.peg_gather_rows(P(x), peg.BF16, T, H, K2, P(b["slot_w"]), P(b["yw"]), E2 * C2, None, st) == 0
+
+
+_SNAP2 = ("top", "w", "top2", "w2", "idx", "bid", "tpe", "bins", "slot", "po", "re", "gp", "flags", "y", "comb",
+          "wg", "idx_w", "bid_w", "tpe_w", "bins_w", "slot_w", "yw")
+
+
+def _dev2(arrs):
+    return [to_dev(a, W.BF16) if i in (4, 5) else to_dev(a) for i, a in enumerate(arrs)]
+
+
+def test_graph_other_entry_points_match_eager():
+    inp = _dev2(_inputs2(0))
+    cap = _buffers2()
+    _step2(inp, cap)  # warm up before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _step2(inp, cap)
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        for dst, src in zip(inp, _dev2(_inputs2(seed))):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: cap[k].clone() for k in _SNAP2}
+        eager = _buffers2()
+        _step2(inp, eager)
+        torch.cuda.synchronize()
+        for k in _SNAP2:
+            g, e = got[k], eager[k]
+            if g.dtype == torch.bfloat16:
+                g, e = g.view(torch.int16), e.view(torch.int16)
+            assert torch.equal(g, e), (seed, k)
+        assert int(got["flags"].item()) == 0
