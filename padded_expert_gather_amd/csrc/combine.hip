@@ -71,10 +71,11 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     constexpr int N = L::N;
     constexpr int KB = KR < kKBatch ? KR : kKBatch;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = xcd_block(blockIdx.x, gridDim.x) * TokenMap<WPT>::kTokensPerBlock + w / WPT;
+    const int64_t gw = xcd_block(blockIdx.x, gridDim.x) * (kBlock / kWave) + w;  // wave of the launch
+    const int64_t t = gw / WPT;  // WPT 8 or 16: a token spans 2 or 4 blocks
     if (t >= T) return;  // no barrier in this kernel
     const int lane = lane_id();
-    const int64_t c_begin = (w % WPT) * slice;
+    const int64_t c_begin = (gw % WPT) * slice;
     const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
     const int64_t R = expert_rows(static_rows, padded_bins, E);
     const int32_t* my_rows = slot_row + t * K;
