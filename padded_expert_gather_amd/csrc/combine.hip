@@ -372,6 +372,11 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
 #ifndef PEG_COMBINE_WPT_SHORT
 #define PEG_COMBINE_WPT_SHORT 2
 #endif
+// ... and above it PEG_COMBINE_WPT_LONG (T8192 H7168 K8: 102.8 us at 8 waves,
+// a token over two blocks, against 104.9 at 4).
+#ifndef PEG_COMBINE_WPT_LONG
+#define PEG_COMBINE_WPT_LONG 8
+#endif
 #ifndef PEG_WGRAD_UMAX
 #define PEG_WGRAD_UMAX 2
 #endif
@@ -387,7 +392,7 @@ struct RowShape {
 };
 static RowShape combine_shape(int32_t K, int64_t nch) {
     if (K <= 2) return RowShape{PEG_COMBINE_WPT_K2, PEG_COMBINE_UMAX_K2};
-    return RowShape{nch <= PEG_COMBINE_SPLIT ? PEG_COMBINE_WPT_SHORT : PEG_COMBINE_WPT, PEG_COMBINE_UMAX};
+    return RowShape{nch <= PEG_COMBINE_SPLIT ? PEG_COMBINE_WPT_SHORT : PEG_COMBINE_WPT_LONG, PEG_COMBINE_UMAX};
 }
 // K > 2 with rows above PEG_WGRAD_SPLIT vectors: PEG_WGRAD_WPT_LONG waves
 // per token (T8192 H7168 K8: wgrad 90.5 us at 4 waves against 94.9 at 2,
@@ -448,11 +453,8 @@ static peg_status combine_go(int wpt, dim3 grid, hipStream_t s, const uint8_t* y
     return launch(combine_kernel<DT, VEC, U, WPT, KR>, grid, dim3(kBlock), 0, s, y, out, nch, q, T, K, slot_row, \
                   w, ra.static_rows, ra.padded_bins, E)
     if (K <= 2) PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT_K2, 2);
-#if PEG_COMBINE_WPT_SHORT != PEG_COMBINE_WPT
     if (wpt == PEG_COMBINE_WPT_SHORT) PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT_SHORT, kRowsFast);
-#endif
-    (void)wpt;
-    PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT, kRowsFast);
+    PEG_COMBINE_LAUNCH(PEG_COMBINE_WPT_LONG, kRowsFast);
 #undef PEG_COMBINE_LAUNCH
 }
 
