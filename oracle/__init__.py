@@ -182,7 +182,7 @@ def gather(x, r, layout, capacity=None, rows=None, R=None):
     ``rows``: optional list of expert-tensor rows to return (a sample)."""
     x = np.ascontiguousarray(x)
     T = x.shape[0]
-    row_bytes = x.strides[0] if x.ndim == 2 else x.itemsize
+    row_bytes = x.shape[1] * x.itemsize  # numpy reports stride 0 for an empty batch
     H = x.shape[1]
     if R is None:
         R = expert_rows(r, layout, capacity)

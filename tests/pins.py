@@ -318,6 +318,23 @@ def pin_gather_numpy(o):
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"padded gather m={m}"
 
 
+def pin_gather_empty_batch(o):
+    """No tokens (T = 0): the binned tensor is E * C rows of zeros, the padded
+    one has no rows, whatever memory the output is allocated in (freed
+    non-zero buffers of the same size are reused by the allocator)."""
+    for H, dtype in ((2, W.F32), (5, W.BF16)):
+        x = W.normal(np.random.default_rng(33), (0, H), dtype)
+        top = np.zeros((0, 3), np.int32)
+        for E, C in ((129, 1), (4, 7)):
+            r = o.route_prep(top, E, pad_multiple=4)
+            for _ in range(3):
+                junk = np.full((E * C, H), 0x55, x.dtype)
+                del junk
+                got = o.gather(x, r, W.BINNED, C)
+                assert got.shape == (E * C, H) and not np.any(got.view(np.uint8)), "empty binned gather"
+            assert o.gather(x, r, W.PADDED).shape == (0, H)
+
+
 def pin_gather_bits_and_identity(o):
     """Gather is a bit copy (NaN payloads, -0.0, subnormals survive), and with
     E = 1, K = 1, C = T (or m = 1) it reproduces x exactly."""
@@ -673,7 +690,8 @@ def pin_validate(o):
 
 
 ALL_PINS = [pin_bf16_rounding, pin_f16_rounding, pin_widening, pin_route_prep_numpy, pin_route_prep_exhaustive,
-            pin_route_prep_invariants, pin_golden, pin_gather_numpy, pin_gather_bits_and_identity,
+            pin_route_prep_invariants, pin_golden, pin_gather_numpy, pin_gather_empty_batch,
+            pin_gather_bits_and_identity,
             pin_scatter_closed_form, pin_scatter_random_y, pin_wgrad_autograd, pin_wgrad_closed_form,
             pin_sampled_tokens, pin_combine_backward, pin_windows, pin_compaction, pin_router_selection,
             pin_router_weights_library, pin_router_matches_workload_router, pin_router_closed_forms, pin_validate]
