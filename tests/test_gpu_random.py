@@ -1,0 +1,75 @@
+"""GPU: seeded random shapes through the whole path, against the oracle.
+
+Each seed draws a layout, element type, T (0..3000), K (1..16, at most E),
+E (1..300), H (1..700), a capacity or padding multiple, a share of absent
+routes and a skew, then checks route_prep, both forms of the gather, the
+combine, wgrad and the combine backward with the rules of the edge tests:
+integer outputs and gathers bit for bit, floating outputs within the
+tolerance of tests/gpu_util.py. The seed is in the test id, so a failure
+names its case.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import padded_expert_gather_amd as peg
+import workloads as W
+from gpu_util import assert_close, bits_equal, to_dev, to_host
+from test_gpu_edge import check_combine_backward
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(150))
+
+
+def _draw(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([1, 2, 3, 8, 16, 33, 64, 129, 256, 300]))
+    K = int(min(E, rng.choice([1, 2, 3, 4, 8, 9, 16])))
+    T = int(rng.choice([0, 1, 7, 100, 777, 2048, 3000]))
+    H = int(rng.choice([1, 2, 3, 8, 33, 64, 250, 512, 700]))
+    dtype = int(rng.choice([W.F32, W.BF16, W.F16]))
+    layout = int(rng.choice([W.BINNED, W.PADDED]))
+    cap = int(rng.integers(1, max(2, 2 * T * K // E + 2))) if layout == W.BINNED else None
+    m = int(rng.choice([1, 2, 8, 64, 128])) if layout == W.PADDED else None
+    none_frac = float(rng.choice([0.0, 0.1, 0.5]))
+    skew = float(rng.choice([0.0, 0.3, 1.0]))
+    return rng, dict(T=T, K=K, E=E, H=H, dtype=dtype, layout=layout, cap=cap, m=m, none_frac=none_frac, skew=skew)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_shape(seed):
+    rng, c = _draw(seed)
+    T, K, E, H, dtype, layout, cap, m = (c[k] for k in ("T", "K", "E", "H", "dtype", "layout", "cap", "m"))
+    print(f"[random] seed {seed}: {c}", flush=True)
+    top, w = W.random_routing(rng, T, K, E, none_frac=c["none_frac"], skew=c["skew"])
+    x = W.normal(rng, (T, H), dtype)
+    grad = W.normal(rng, (T, H), dtype)
+    ro = oracle.route_prep(top, E, pad_multiple=m)
+    rg = peg.route_prep(to_dev(top), E, capacity=cap, pad_multiple=m)
+    bits_equal(to_host(rg.indices), ro.indices, "indices")
+    bits_equal(to_host(rg.bin_ids), ro.bin_ids, "bin_ids")
+    bits_equal(to_host(rg.tokens_per_expert), ro.tokens_per_expert, "tokens_per_expert")
+    bits_equal(to_host(rg.bins), ro.bins, "bins")
+    if m is not None:
+        bits_equal(to_host(rg.padded_bins), ro.padded_bins, "padded_bins")
+    rows = oracle.assignment_rows(ro, layout, cap)
+    bits_equal(to_host(rg.slot_row), rows, "slot_row")
+    R = oracle.expert_rows(ro, layout, cap)
+    xg = to_dev(x, dtype)
+    gather = peg.gather_binned if layout == W.BINNED else peg.gather_padded
+    yo = oracle.gather(x, ro, layout, cap)
+    yg = gather(xg, rg)
+    bits_equal(to_host(yg), yo, "gather")
+    bits_equal(to_host(gather(xg, rg, use_slot_row=False)), yo, "gather (rebuilt map)")
+    if T == 0:
+        return
+    wg = to_dev(w.reshape(-1))
+    so, S = oracle.scatter_combine(yo, dtype, ro, layout, cap, weights=w.reshape(-1), with_scale=True)
+    assert_close(to_host(peg.scatter_combine(yg, rg, weights=wg)), so, S, dtype, "combine")
+    yr = W.expert_tensor_rows(rng, R, H, dtype, used_rows=rows[rows >= 0])
+    yrg = to_dev(yr, dtype)
+    gg = to_dev(grad, dtype)
+    wo, WS = oracle.wgrad(yr, grad, dtype, ro, layout, cap, with_scale=True)
+    assert_close(to_host(peg.wgrad(yrg, gg, rg)), wo, WS, W.F32, "wgrad")
+    check_combine_backward(yrg, yr, grad, gg, w, wg, ro, rg, layout, cap, dtype, R)
