@@ -1,5 +1,8 @@
 """GPU: seeded random shapes through the whole path, against the oracle.
 
+(A second set of seeds draws shapes for the compaction and its backward,
+the router gating alone and fused with route_prep, and row windows.)
+
 Each seed draws a layout, element type, T (0..3000), K (1..16, at most E),
 E (1..300), H (1..700), a capacity or padding multiple, a share of absent
 routes and a skew, then checks route_prep, both forms of the gather, the
@@ -72,3 +75,53 @@ def test_random_shape(seed):
     wo, WS = oracle.wgrad(yr, grad, dtype, ro, layout, cap, with_scale=True)
     assert_close(to_host(peg.wgrad(yrg, gg, rg)), wo, WS, W.F32, "wgrad")
     check_combine_backward(yrg, yr, grad, gg, w, wg, ro, rg, layout, cap, dtype, R)
+
+
+def _draw_aux(seed):
+    rng = np.random.default_rng(5000 + seed)
+    E = int(rng.choice([1, 2, 5, 8, 16, 64, 100, 256, 1024]))
+    K = int(min(E, rng.choice([1, 2, 3, 8, 16])))
+    T = int(rng.choice([0, 1, 9, 500, 3000]))
+    return rng, T, K, E
+
+
+@pytest.mark.parametrize("seed", list(range(60)))
+def test_random_compaction_router_windows(seed):
+    """Compaction (and its backward), router gating alone and fused with
+    route_prep, and routing into row windows, at one random shape each."""
+    rng, T, K, E = _draw_aux(seed)
+    print(f"[random aux] seed {seed}: T{T} K{K} E{E}", flush=True)
+    # compaction of a dense map with 0..max routes per row (max can exceed topk)
+    dtype = int(rng.choice([W.F32, W.BF16, W.F16]))
+    rmap = W.routing_map_rows(rng, T, E, int(min(E, K + rng.integers(0, 3))))
+    probs = W.normal(rng, (T, E), dtype)
+    po, re = oracle.routing_map_compact(probs, dtype, rmap, K)
+    pg, rg_ = peg.routing_map_compact(to_dev(probs, dtype), to_dev(rmap), K)
+    bits_equal(to_host(rg_), re, "route_experts")
+    bits_equal(to_host(pg), po, "probs_out")
+    gco = rng.standard_normal((T, K)).astype(np.float32)
+    bits_equal(to_host(peg.routing_map_compact_backward(to_dev(gco), rg_, E)),
+               oracle.routing_map_compact_backward(gco, re, E), "compaction backward")
+    # router gating: selection bit for bit, weights within the router tolerance
+    from test_gpu_router import check_weights
+    logits = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    gating = int(rng.choice([peg.SOFTMAX, peg.SIGMOID]))
+    norm = bool(rng.integers(0, 2))
+    to, wo = oracle.router_topk(logits, W.F32, K, gating, norm)
+    tg, wg = peg.router_topk(to_dev(logits), K, gating=gating, normalize=norm)
+    bits_equal(to_host(tg), to, "router top_experts")
+    check_weights(to_host(wg), wo, "router weights")
+    cap = int(rng.integers(1, 2 * max(1, T * K // E) + 2))
+    rf, tf, wf = peg.route_prep_logits(to_dev(logits), K, capacity=cap, gating=gating, normalize=norm)
+    bits_equal(to_host(tf), to, "fused top_experts")
+    check_weights(to_host(wf), wo, "fused weights")
+    ro = oracle.route_prep(to, E)
+    bits_equal(to_host(rf.indices), ro.indices, "fused indices")
+    bits_equal(to_host(rf.bins), ro.bins, "fused bins")
+    bits_equal(to_host(rf.slot_row), oracle.assignment_rows(ro, W.BINNED, cap), "fused slot_row")
+    # row windows of the same routing
+    base = rng.integers(0, 5000, size=E).astype(np.int32)
+    limit = (base + rng.integers(0, 2 * max(1, T * K // E) + 2, size=E)).astype(np.int32)
+    rw = peg.route_prep_windows(to_dev(to), E, to_dev(base), to_dev(limit))
+    bits_equal(to_host(rw.indices), ro.indices, "windows indices")
+    bits_equal(to_host(rw.slot_row), oracle.assignment_rows_windows(ro, base, limit), "windows slot_row")
