@@ -1,15 +1,14 @@
 """GPU: seeded random shapes through the whole path, against the oracle.
 
-(A second set of seeds draws shapes for the compaction and its backward,
-the router gating alone and fused with route_prep, and row windows.)
-
 Each seed draws a layout, element type, T (0..3000), K (1..16, at most E),
 E (1..300), H (1..700), a capacity or padding multiple, a share of absent
 routes and a skew, then checks route_prep, both forms of the gather, the
 combine, wgrad and the combine backward with the rules of the edge tests:
 integer outputs and gathers bit for bit, floating outputs within the
-tolerance of tests/gpu_util.py. The seed is in the test id, so a failure
-names its case.
+tolerance of tests/gpu_util.py. A second set of seeds draws shapes for the
+compaction and its backward, the router gating alone and fused with
+route_prep, and row windows. The seed is in the test id, so a failure names
+its case.
 """
 import numpy as np
 import pytest
