@@ -40,7 +40,9 @@ def test_windows_match_oracle(T, K, E):
 
 
 @pytest.mark.parametrize("T,K,E,H,C,cuts", [(4096, 2, 8, 512, 1100, (1000, 1001, 3000)),
-                                           (2000, 8, 64, 96, 230, (700, 1300))])
+                                           (2000, 8, 64, 96, 230, (700, 1300)),
+                                           (1000, 2, 8, 6144, 300, (333,)),     # long rows: a token over 2 blocks
+                                           (600, 4, 16, 4100, 180, (1, 599))])
 def test_shards_reproduce_one_call(T, K, E, H, C, cuts):
     print(f"[shards] T{T} K{K} E{E} H{H} C{C}", flush=True)
     rng = np.random.default_rng(7 * T + E)
