@@ -8,7 +8,8 @@ Workloads (workloads.config):
   5 binned bf16 T32768 H3584 E64 K8 C4096  (Qwen2-MoE-57B-shaped, heavy skew)
 
 Every index output is compared bit for bit in full. Gathers: full bit
-comparison for 1-2; for 3-5 every kept row is checked against its token row
+comparison for 1-2; for 3-5 (seeds 0-4 at full width, and seeds 1-4 once
+more with narrow rows) every kept row is checked against its token row
 on the device, every other row is checked to be zero, and a row sample is
 compared with the oracle. Combine / wgrad: the oracle on sampled tokens
 (independent random y with NaN in unused rows, and y = gather(x)), plus the
@@ -103,17 +104,17 @@ def _check_gather_full(yg, xg, rows, K, what):
     return kept
 
 
-@pytest.mark.parametrize("cid", [3, 4, 5])
-def test_large_config(cid):
-    """Workloads 3-5 (seed 0) at full size."""
-    print(f"[config {cid}] generating", flush=True)
-    wl = W.config(cid, 0)
+@pytest.mark.parametrize("cid,seed", [(c, s) for s in range(5) for c in (3, 4, 5)])
+def test_large_config(cid, seed):
+    """Workloads 3-5, seeds 0-4, at full size."""
+    print(f"[config {cid} seed {seed}] generating", flush=True)
+    wl = W.config(cid, seed)
     ro, rg, rows, cap, w_o, w_g = _prep(wl)
     print(f"[config {cid}] routing ok; n={ro.n}", flush=True)
     if cid == 3:
         counts = np.asarray(ro.tokens_per_expert)
         assert int(np.sum(counts > wl.capacity)) == 2 and int(np.sum(counts == 0)) == 1
-    rng = np.random.default_rng(1000 + cid)
+    rng = np.random.default_rng(1000 + cid + 100 * seed)
     xg = to_dev(wl.x, wl.dtype)
     gg = to_dev(wl.grad, wl.dtype)
     yg = peg.gather_binned(xg, rg) if wl.layout == W.BINNED else peg.gather_padded(xg, rg)
@@ -193,7 +194,7 @@ def test_large_config(cid):
 def test_large_config_routing_seeds(cid, seed):
     """Workloads 3-5, seeds 1-4: the routing at full size (compaction for 4)
     bit for bit, and a gather of narrow rows (H = 40) through it, every row
-    checked against its token (full-width rows are covered by seed 0)."""
+    checked against its token (full-width rows: test_large_config)."""
     print(f"[config {cid} seed {seed}] routing", flush=True)
     wl = W.config(cid, seed, with_rows=False)
     ro, rg, rows, cap, _, _ = _prep(wl)
