@@ -406,7 +406,6 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the data path is a "
               f"single-GPU library; it has no multi-GPU code)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np  # noqa: F401
     import torch
     import padded_expert_gather_amd as peg
     import workloads as W
