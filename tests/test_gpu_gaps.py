@@ -1,5 +1,6 @@
 """GPU: zeroing of the gap rows of large expert tensors (hundreds of MB,
-mostly gap), against the oracle's gather, bit for bit.
+mostly gap), against the oracle's gather, bit for bit; and one expert tensor
+past 2^31 bytes through the gather, the combine and wgrad.
 
 Every output buffer is filled with 0xFF bytes first, so a gap row that is
 not written shows up as a mismatch. Cases: 16-, 8-, 4- and 2-byte row
@@ -109,3 +110,52 @@ def test_large_gaps_cut_buffer():
     host = to_host(buf)
     bits_equal(host[:small], oracle.gather(x, ro, W.PADDED)[:small], "cut padded gather")
     assert (host[small:].view(np.uint8) == 0xFF).all(), "rows past the buffer were written"
+
+
+def test_tensor_beyond_2gib():
+    """An expert tensor of 2.6 GB (byte offsets past 2^31): the gather, the
+    combine and wgrad through it, checked on the device against the token
+    rows (gather: every row; combine and wgrad: their closed forms on every
+    token) and against the oracle on a row sample."""
+    print("[beyond 2 GiB]", flush=True)
+    rng = np.random.default_rng(21)
+    T, K, E, H, C = 65536, 4, 64, 4096, 5000
+    assert E * C * H * 2 > 2 ** 31
+    top, w = W.random_routing(rng, T, K, E, none_frac=0.02, skew=0.2)
+    x = W.normal(rng, (T, H), W.BF16)
+    ro = oracle.route_prep(top, E)
+    rg = peg.route_prep(to_dev(top), E, capacity=C)
+    rows = oracle.assignment_rows(ro, W.BINNED, C)
+    bits_equal(to_host(rg.slot_row), rows, "slot_row")
+    xg = to_dev(x, W.BF16)
+    y = _filled(E * C, H, W.BF16)
+    peg.gather_binned(xg, rg, out=y)
+    kept = np.flatnonzero(rows >= 0)
+    rk = torch.from_numpy(rows[kept].astype(np.int64)).to(DEV)
+    tk = torch.from_numpy((kept // K).astype(np.int64)).to(DEV)
+    yv, xv = y.view(torch.int16), xg.view(torch.int16)
+    for lo in range(0, len(kept), 65536):  # kept rows against their tokens, in slices
+        assert torch.equal(yv[rk[lo:lo + 65536]], xv[tk[lo:lo + 65536]]), "a kept row differs from its token"
+    gap = torch.ones(E * C, dtype=torch.bool, device=DEV)
+    gap[rk] = False
+    assert int(yv[gap].count_nonzero().item()) == 0, "a gap row is not zero"
+    sample = np.unique(np.concatenate([[0, E * C - 1], rng.choice(E * C, 512, replace=False),
+                                       np.arange(E) * C + C - 1])).astype(np.int64)
+    bits_equal(to_host(y[torch.from_numpy(sample).to(DEV)]), oracle.gather(x, ro, W.BINNED, C, rows=sample),
+               "gather sample")
+    # combine and wgrad through the 2.6 GB tensor: closed forms on every token
+    wg = to_dev(w.reshape(-1))
+    keptmask = torch.from_numpy((rows >= 0).reshape(T, K)).to(DEV)
+    wsum = torch.where(keptmask, wg.reshape(T, K), torch.zeros((), device=DEV)).sum(1)
+    xf = xg.float()
+    comb = peg.scatter_combine(y, rg, weights=wg).float()
+    want = wsum[:, None] * xf
+    assert bool(((comb - want).abs() <= 2e-2 * want.abs() + 1e-5 * wsum.abs()[:, None] * xf.abs()).all()), \
+        "combine closed form"
+    grad = W.normal(rng, (T, H), W.BF16)
+    gg = to_dev(grad, W.BF16)
+    wgr = peg.wgrad(y, gg, rg)
+    prod = xf * gg.float()
+    wwant = torch.where(keptmask, prod.sum(1)[:, None], torch.zeros((), device=DEV))
+    assert bool(((wgr - wwant).abs() <= 1e-5 * wwant.abs() + 2e-5 * prod.abs().sum(1)[:, None]).all()), \
+        "wgrad closed form"
