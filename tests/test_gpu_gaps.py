@@ -1,6 +1,7 @@
 """GPU: zeroing of the gap rows of large expert tensors (hundreds of MB,
 mostly gap), against the oracle's gather, bit for bit; and one expert tensor
-past 2^31 bytes through the gather, the combine and wgrad.
+past 2^31 bytes through the gather, the combine, wgrad and the combine
+backward.
 
 Every output buffer is filled with 0xFF bytes first, so a gap row that is
 not written shows up as a mismatch. Cases: 16-, 8-, 4- and 2-byte row
@@ -114,9 +115,10 @@ def test_large_gaps_cut_buffer():
 
 def test_tensor_beyond_2gib():
     """An expert tensor of 2.6 GB (byte offsets past 2^31): the gather, the
-    combine and wgrad through it, checked on the device against the token
-    rows (gather: every row; combine and wgrad: their closed forms on every
-    token) and against the oracle on a row sample."""
+    combine, wgrad and the combine backward through it, checked on the device
+    against the token rows (gather and dy: every row; combine and wgrad:
+    their closed forms on every token) and against the oracle on a row
+    sample."""
     print("[beyond 2 GiB]", flush=True)
     rng = np.random.default_rng(21)
     T, K, E, H, C = 65536, 4, 64, 4096, 5000
@@ -159,3 +161,16 @@ def test_tensor_beyond_2gib():
     wwant = torch.where(keptmask, prod.sum(1)[:, None], torch.zeros((), device=DEV))
     assert bool(((wgr - wwant).abs() <= 1e-5 * wwant.abs() + 2e-5 * prod.abs().sum(1)[:, None]).all()), \
         "wgrad closed form"
+    # the combine backward writes a second 2.6 GB tensor: kept rows w * dout
+    # (one rounding, computed here by torch), gap rows zero; its wgrad equals
+    # the wgrad kernel's bit for bit
+    del comb, want, prod
+    dyg, wgb = peg.combine_backward(y, gg, rg, weights=wg, dy_rows=E * C)
+    kept_t = torch.from_numpy(kept.astype(np.int64)).to(DEV)
+    dv = dyg.view(torch.int16)
+    for lo in range(0, len(kept), 65536):
+        sl = slice(lo, lo + 65536)
+        want_rows = (wg[kept_t[sl]].unsqueeze(1) * gg[kept_t[sl] // K].float()).to(torch.bfloat16)
+        assert torch.equal(dv[rk[sl]], want_rows.view(torch.int16)), "backward dy kept rows"
+    assert int(dv[gap].count_nonzero().item()) == 0, "backward dy gap rows"
+    assert torch.equal(wgb, wgr), "fused wgrad == wgrad kernel"
