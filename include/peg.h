@@ -185,6 +185,8 @@ peg_status peg_gather_padded(const void* x, int32_t dtype, int64_t T, int64_t H,
  * padding, or dropped are never read. A token with no kept route gets a
  * zero row.
  *   y [R, H] of dtype (expert tensor in `layout`); out [T, H] of dtype.
+ *   y may be NULL for a padded tensor of no rows (padded_bins[E-1] = 0):
+ *       then no row is read (and every output row is zero).
  *   weights [T*K] f32 by assignment id, or NULL (every factor is 1).
  *   capacity: binned only. padded_bins: padded only. indices/bin_ids/bins/
  *   padded_bins are read only when slot_row is NULL.
@@ -205,6 +207,7 @@ peg_status peg_scatter_combine(const void* y, int32_t dtype, int32_t layout, int
  * wgrad[a] = sum_h y[row(a), h] * grad[a/K, h] for every kept assignment a,
  * accumulated in fp32; wgrad[a] = 0 for dropped or unrouted assignments.
  *   y [R, H] and grad [T, H] both of dtype; wgrad [T*K] f32, fully written.
+ *   y may be NULL for a padded tensor of no rows (then every wgrad is 0).
  * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, ALIGNMENT, WORKSPACE, LAUNCH.
  */
 peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int32_t layout, int64_t T,
@@ -228,7 +231,8 @@ peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int32_t lay
  *   wgrad[a]   = <y[row(a)], dout[a/K]> as peg_wgrad.
  *   y [R, H], dout [T, H], dy [dy_rows, H], all of dtype; weights [T*K] f32
  *   or NULL; wgrad [T*K] f32, fully written. R = E*C (binned) or
- *   padded_bins[E-1] (padded). Rows of dy at or past dy_rows are never
+ *   padded_bins[E-1] (padded); y may be NULL for a padded tensor of no rows
+ *   (every wgrad is then 0). Rows of dy at or past dy_rows are never
  *   written (a route whose row is there gets no dy row; its wgrad is still
  *   computed). The other arguments are as for peg_wgrad.
  * Errors: NULL_ARG, BAD_SHAPE (also dy_rows < 0), BAD_DTYPE, ALIGNMENT,

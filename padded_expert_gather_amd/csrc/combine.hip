@@ -46,7 +46,11 @@ constexpr int kWgradKBatch = PEG_WGRAD_KBATCH;  // the same for wgrad and the co
 #define PEG_WGRAD_OCCUPANCY
 #endif
 
-__device__ __forceinline__ int64_t expert_rows(int64_t static_rows, const int32_t* padded_bins, int32_t E) {
+// Rows of the expert tensor y; none when y is NULL (a padded tensor of no
+// rows), so that no row is read.
+__device__ __forceinline__ int64_t expert_rows(const void* y, int64_t static_rows, const int32_t* padded_bins,
+                                               int32_t E) {
+    if (!y) return 0;
     return padded_bins ? (int64_t)padded_bins[E - 1] : static_rows;
 }
 
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     const int lane = lane_id();
     const int64_t c_begin = (gw % WPT) * slice;
     const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
-    const int64_t R = expert_rows(static_rows, padded_bins, E);
+    const int64_t R = expert_rows(y, static_rows, padded_bins, E);
     const int32_t* my_rows = slot_row + t * K;
     const float* my_w = weights ? weights + t * K : nullptr;
     int r8[KR];
@@ -190,7 +194,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
     const int lane = lane_id();
     const int64_t c_begin = (w % WPT) * slice;
     const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
-    const int64_t R = expert_rows(static_rows, padded_bins, E);
+    const int64_t R = expert_rows(y, static_rows, padded_bins, E);
     const int32_t* my_rows = slot_row + (active ? t : 0) * K;
     const int64_t row_bytes = nch * VEC;
     const uint8_t* g_row = grad + (active ? t : 0) * row_bytes;
@@ -576,7 +580,7 @@ PEG_API peg_status peg_scatter_combine(const void* y, int32_t dtype, int32_t lay
                                        const int32_t* slot_row, const float* weights, void* out, void* ws,
                                        size_t ws_bytes, void* stream) {
     PEG_CHECK(check_common(dtype, layout, T, H, K, E, capacity, padded_bins));
-    if (T > 0 && (!y || !out)) return PEG_ERR_NULL_ARG;
+    if (T > 0 && ((!y && layout == PEG_BINNED) || !out)) return PEG_ERR_NULL_ARG;
     const int eb = elem_bytes(dtype);
     if (!aligned(y, eb) || !aligned(out, eb) || (weights && !aligned(weights, 4))) return PEG_ERR_ALIGNMENT;
     const int vec = pick_vec(H * eb, eb, y, out);
@@ -598,7 +602,7 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
                              const int32_t* bins, const int32_t* padded_bins, const int32_t* slot_row,
                              float* wgrad, void* ws, size_t ws_bytes, void* stream) {
     PEG_CHECK(check_common(dtype, layout, T, H, K, E, capacity, padded_bins));
-    if (T > 0 && (!y || !grad || !wgrad)) return PEG_ERR_NULL_ARG;
+    if (T > 0 && ((!y && layout == PEG_BINNED) || !grad || !wgrad)) return PEG_ERR_NULL_ARG;
     const int eb = elem_bytes(dtype);
     if (!aligned(y, eb) || !aligned(grad, eb) || !aligned(wgrad, 4)) return PEG_ERR_ALIGNMENT;
     const int vec = pick_vec(H * eb, eb, y, grad);
@@ -625,7 +629,8 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
                                         int64_t dy_rows, float* wgrad, void* ws, size_t ws_bytes, void* stream) {
     PEG_CHECK(check_common(dtype, layout, T, H, K, E, capacity, padded_bins));
     if (dy_rows < 0 || dy_rows > kMaxAssign) return PEG_ERR_BAD_SHAPE;
-    if (!bins || (T > 0 && (!y || !dout || !wgrad)) || (dy_rows > 0 && !dy)) return PEG_ERR_NULL_ARG;
+    if (!bins || (T > 0 && ((!y && layout == PEG_BINNED) || !dout || !wgrad)) || (dy_rows > 0 && !dy))
+        return PEG_ERR_NULL_ARG;
     const int eb = elem_bytes(dtype);
     if (!aligned(y, eb) || !aligned(dout, eb) || !aligned(dy, eb) || !aligned(wgrad, 4) ||
         (weights && !aligned(weights, 4)))

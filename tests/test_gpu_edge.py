@@ -64,6 +64,8 @@ CASES = [
     _case("all_one_expert_padded", 70, 2, 8, 64, W.BF16, P, m=32, one_expert=5),
     _case("tokens_all_dropped", 200, 2, 4, 64, W.BF16, B, cap=10),
     _case("rows_all_none", 50, 2, 4, 64, W.BF16, P, m=4, none_frac=0.7),
+    _case("padded_no_rows", 5, 2, 4, 64, W.BF16, P, m=4, none_frac=1.0),  # a padded tensor of 0 rows
+    _case("binned_no_routes", 5, 2, 4, 64, W.F16, B, cap=3, none_frac=1.0),
     _case("E300_items4", 900, 2, 300, 16, W.BF16, P, m=4, skew=0.01),
     _case("E1024_items2", 1500, 2, 1024, 16, W.BF16, B, cap=3),
     _case("E1024_scan_launch", 10000, 2, 1024, 8, W.BF16, P, m=2),
