@@ -180,7 +180,7 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
         const int64_t nz = (int64_t)gridDim.x - token_blocks;
         int64_t role_index;
         if (gap_role(blockIdx.x, gridDim.x, nz, &role_index)) {
-            zero_gap_rows<VEC>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins, role_index, nz);
+            zero_gap_rows<VEC, PEG_NT_STORE_DY_ZERO>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins, role_index, nz);
             return;
         }
         tblock = role_index;
@@ -249,12 +249,12 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
                                 if (r < 0 || r >= dy_rows) continue;
                                 uint8_t* drow = dy + (int64_t)r * row_bytes;
                                 if constexpr (DY == 1) {
-                                    stream_store<VEC>(drow, c, gv[u]);
+                                    stream_store<VEC, PEG_NT_STORE_DY>(drow, c, gv[u]);
                                 } else {
                                     float o[N];
 #pragma unroll
                                     for (int i = 0; i < N; ++i) o[i] = w8[kb + kk] * g[i];
-                                    stream_store<VEC>(drow, c, L::pack(o));
+                                    stream_store<VEC, PEG_NT_STORE_DY>(drow, c, L::pack(o));
                                 }
                             }
                         }
@@ -428,8 +428,11 @@ static RowShape wgrad_shape(int32_t K, int64_t nch) {
 #ifndef PEG_BACKWARD_WPT
 #define PEG_BACKWARD_WPT PEG_WGRAD_WPT
 #endif
+// The combine backward with K > 2 keeps 4 vectors per lane per pass
+// (T8192 H7168 K8: 250.8 us against 262.2 at 2; T32768 H3584 K8 509.9
+// against 511.1).
 #ifndef PEG_BACKWARD_UMAX
-#define PEG_BACKWARD_UMAX PEG_WGRAD_UMAX
+#define PEG_BACKWARD_UMAX 4
 #endif
 #ifndef PEG_BACKWARD_WPT_LONG
 #define PEG_BACKWARD_WPT_LONG PEG_WGRAD_WPT_LONG

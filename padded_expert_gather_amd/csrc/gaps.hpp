@@ -70,7 +70,7 @@ inline int64_t gap_blocks(int64_t max_gap_rows, int64_t nch) {
 // (out_rows rows of nch VEC-byte vectors). Binned: expert e's rows
 // [e*C + min(count, C), (e+1)*C); padded: [pstart(e) + count, padded_bins[e]).
 // Whole block must call it (contains barriers).
-template <int VEC>
+template <int VEC, bool NT = PEG_NT_STORE_ZERO>
 __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t nch, int64_t out_rows,
                                               int32_t layout, int32_t E, int32_t capacity,
                                               const int32_t* __restrict__ bins,
@@ -130,7 +130,7 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
             if (u >= units) break;
             while ((int64_t)gpre[e + 1] * nch <= u) ++e;
             const int64_t shift = (int64_t)gstart[e] * nch - (int64_t)gpre[e] * nch;
-            stream_store<VEC, PEG_NT_STORE_ZERO>(out, shift + u, z);
+            stream_store<VEC, NT>(out, shift + u, z);
         }
     }
     return;
@@ -155,7 +155,7 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
 #pragma unroll
             for (int j = 0; j < kZeroUnroll; ++j) {
                 const int64_t uu = u + (int64_t)j * kBlock;
-                if (uu < seg_end) stream_store<VEC, PEG_NT_STORE_ZERO>(out, shift + uu, z);
+                if (uu < seg_end) stream_store<VEC, NT>(out, shift + uu, z);
             }
         }
         u0 = seg_end > u0 ? seg_end : u0;

@@ -27,7 +27,11 @@ template <> struct VecOf<2> { using T = uint16_t; };
 //                  every row kernel);
 //   PEG_NT_STORE - the gathers' row stores carry it too (off: it costs the
 //                  write-bound gathers up to 17%);
-//   PEG_NT_STORE_COMBINE - the combine's output stores carry it (+7-9%).
+//   PEG_NT_STORE_COMBINE - the combine's output stores carry it (+7-9%);
+//   PEG_NT_STORE_DY - the combine backward's dy row stores carry it (2-8%
+//                  faster on the four model-shaped batches); its zero stores
+//                  of dy's gap rows do not (PEG_NT_STORE_DY_ZERO: up to 10%
+//                  slower with it).
 #ifndef PEG_NT_LOAD
 #define PEG_NT_LOAD 1
 #endif
@@ -36,6 +40,12 @@ template <> struct VecOf<2> { using T = uint16_t; };
 #endif
 #ifndef PEG_NT_STORE_COMBINE
 #define PEG_NT_STORE_COMBINE 1
+#endif
+#ifndef PEG_NT_STORE_DY
+#define PEG_NT_STORE_DY 1
+#endif
+#ifndef PEG_NT_STORE_DY_ZERO
+#define PEG_NT_STORE_DY_ZERO PEG_NT_STORE
 #endif
 
 template <int VEC>
