@@ -269,3 +269,13 @@ def test_plain_c_consumer(tmp_path):
     assert out.returncode == 0, out.stderr
     assert "abi_check ok" in out.stdout
 
+
+
+def test_c_gpu_driver_compiles():
+    """tests/c/gpu_path.c (the plain C driver of the GPU path, run by the GPU
+    tests) builds against the header, the oracle and the HIP runtime; it is
+    only compiled here, not run."""
+    import __graft_entry__ as entry
+    from oracle import build as oracle_build
+    oracle_build.ensure_built()
+    assert os.access(entry.build_c_driver(), os.X_OK)
