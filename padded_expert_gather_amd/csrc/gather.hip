@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
     const uint8_t* __restrict__ x, uint8_t* __restrict__ out, int64_t nch, int64_t slice, int32_t K,
     const int32_t* __restrict__ slot_row, int64_t out_rows, int32_t layout, int32_t E, int32_t capacity,
     const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins, int64_t T, int64_t token_blocks,
-    uint32_t* __restrict__ err_flag) {
+    uint32_t* __restrict__ err_flag, int32_t early) {
     using V = typename VecOf<VEC>::T;
     const int64_t row_bytes = nch * VEC;
 
@@ -48,6 +48,20 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
         const int64_t c_begin = (gw % WPT) * slice;
         const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
         const int32_t* my_rows = slot_row + t * K;
+        const uint8_t* src = x + t * row_bytes;
+        // early: the first pass's token-row loads go out before the row
+        // indices arrive (they do not depend on them), so the two latencies
+        // overlap; otherwise they wait for the indices, and a token whose
+        // routes are all dropped is never read
+        int64_t c0 = c_begin;
+        V v[U];
+        if (early) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u * kWave + lane;
+                if (c < c_end) v[u] = stream_load<VEC>(src, c);
+            }
+        }
         // rows of the token: wave-uniform loads (scalar unit), K <= 8 kept in SGPRs
         int r8[kRowsFast];
 #pragma unroll
@@ -64,15 +78,15 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
             any |= r >= 0 && r < out_rows;
         }
         if (over && err_flag && lane == 0 && gw % WPT == 0) atomicOr(err_flag, PEG_FLAG_OUT_ROWS);
-        if (!any) return;  // token fully dropped: its row is never read
-        const uint8_t* src = x + t * row_bytes;
-        for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
-            V v[U];
+        if (!any) return;  // token fully dropped: nothing is stored
+        if (!early) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t c = c0 + u * kWave + lane;
                 if (c < c_end) v[u] = stream_load<VEC>(src, c);
             }
+        }
+        for (;;) {
 #pragma unroll
             for (int k = 0; k < kRowsFast; ++k) {
                 const int r = r8[k];
@@ -94,6 +108,13 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(
                     if (c < c_end) stream_store<VEC>(dst, c, v[u]);
                 }
             }
+            c0 += (int64_t)kWave * U;
+            if (c0 >= c_end) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u * kWave + lane;
+                if (c < c_end) v[u] = stream_load<VEC>(src, c);
+            }
         }
         return;
     }
@@ -114,6 +135,7 @@ struct GatherArgs {
     const int32_t* padded_bins;
     int64_t T, token_blocks;
     uint32_t* err_flag;
+    int32_t early;
 };
 
 template <int VEC, int WPT>
@@ -121,7 +143,7 @@ static peg_status gather_launch(int u, dim3 grid, hipStream_t s, const GatherArg
 #define PEG_GATHER_U(UU)                                                                                        \
     return launch(gather_kernel<VEC, UU, WPT>, grid, dim3(kBlock), 0, s, a.x, a.out, a.nch, a.slice, a.K,   \
                   a.slot_row, a.out_rows, a.layout, a.E, a.capacity, a.bins, a.padded_bins, a.T, a.token_blocks, \
-                  a.err_flag)
+                  a.err_flag, a.early)
     if (u == 1) PEG_GATHER_U(1);
     if (u == 2) PEG_GATHER_U(2);
     PEG_GATHER_U(4);
@@ -183,7 +205,7 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
     const int64_t slice = wave_slice(nch, wpt);
     const int u = lanes_per_pass(slice);
     const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, slice, K, slot_row, out_rows, layout, E, capacity,
-                       bins, padded_bins, T, tb, err_flag};
+                       bins, padded_bins, T, tb, err_flag, gather_early(T, wpt)};
     return gather_dispatch(wpt, vec, u, grid, s, a);
 }
 
@@ -231,7 +253,7 @@ PEG_API peg_status peg_gather_rows(const void* x, int32_t dtype, int64_t T, int6
     // no gap blocks: the grid holds token blocks only, so the gap arguments
     // are never read
     const GatherArgs a{(const uint8_t*)x, (uint8_t*)out, nch, slice, K, slot_row, out_rows, PEG_BINNED, 1, 1,
-                       nullptr, nullptr, T, tb, err_flag};
+                       nullptr, nullptr, T, tb, err_flag, gather_early(T, wpt)};
     if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
     const dim3 grid((unsigned)tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

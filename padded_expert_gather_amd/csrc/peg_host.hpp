@@ -66,6 +66,17 @@ inline int gather_wpt(int64_t nch, int32_t K) {
     return K <= 2 ? 8 : 4;
 }
 
+// The gather issues a token row's first loads before its row indices arrive
+// when the token waves fit in about two rounds of the chip's wave slots
+// (T4096 H4096 K2, 8192 waves: 17.0 against 17.8 us); with more rounds the
+// indices' latency is hidden by other waves and the early loads slowed the
+// write-bound gathers (T16384 H6144 K2, 131072 waves: 127.8 against 122.1
+// us; T32768 H3584 K8: 401.8 against 396.5; T8192 H7168 K8: even).
+#ifndef PEG_GATHER_EARLY_WAVES
+#define PEG_GATHER_EARLY_WAVES 16384
+#endif
+inline int32_t gather_early(int64_t T, int wpt) { return T * wpt <= PEG_GATHER_EARLY_WAVES ? 1 : 0; }
+
 template <int WPT>
 struct TokenMap {
     static_assert(WPT == 1 || WPT == 2 || WPT == 4 || WPT == 8 || WPT == 16, "waves per token: 1 to 16");
