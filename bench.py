@@ -13,7 +13,9 @@ Printed: one JSON line. ``value`` is the effective HBM bandwidth of the step,
 (algorithmic bytes of gather + combine + wgrad) / (wall time of the step,
 route_prep and compaction included); ``roofline`` is the dominant kernel's
 algorithmic bytes / its average duration (HIP events on its stream);
-``cpu_baseline`` is the CPU oracle on the same workload. ``backward`` times,
+``cpu_baseline`` is the CPU oracle on the same workload, one thread;
+``cpu_baseline_all_cores`` runs independent whole oracle steps on every host
+thread available (at most 16) at once. ``backward`` times,
 outside the step, the backward of the combine fused with wgrad on the same
 buffers (dy in the expert layout + the routing-weight gradient), and the
 router top-k gating (softmax, renormalised) of the workload's router scores,
@@ -78,6 +80,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: enough for 2 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the all-cores CPU-oracle leg (0: the host's CPUs, at most 16; 1: skip it)")
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
     ap.add_argument("--no-router", action="store_true", help="skip timing the router gating")
@@ -345,24 +349,30 @@ def backward_bytes(wl, sz, s):
     return sz["N"] * H * s + sz["U"] * H * s + sz["R"] * H * s + 12 * T * K
 
 
+def oracle_step(wl, W):
+    """One whole step of the CPU oracle on the workload: compaction (if the
+    workload has a routing map), route_prep, gather, combine, wgrad."""
+    import oracle
+    if wl.routing_map is not None:
+        w, top = oracle.routing_map_compact(wl.probs, W.F32, wl.routing_map, wl.topk)
+    else:
+        w, top = wl.weights, wl.top_experts
+    m = wl.pad_multiple if wl.layout == W.PADDED else None
+    cap = wl.capacity if wl.layout == W.BINNED else None
+    r = oracle.route_prep(top, wl.E, pad_multiple=m)
+    y = oracle.gather(wl.x, r, wl.layout, cap)
+    oracle.scatter_combine(y, wl.dtype, r, wl.layout, cap, weights=w.reshape(-1))
+    oracle.wgrad(y, wl.grad, wl.dtype, r, wl.layout, cap)
+
+
 def cpu_baseline(wl, W, seconds, bytes_step):
     """The CPU oracle, as it stands, on the same workload: whole steps
     (compaction, route_prep, gather, combine, wgrad) repeated until about
     ``seconds`` of CPU time; single-threaded scalar C."""
-    import oracle
     reps, t_total = 0, 0.0
     while True:
         t0 = time.perf_counter()
-        if wl.routing_map is not None:
-            w, top = oracle.routing_map_compact(wl.probs, W.F32, wl.routing_map, wl.topk)
-        else:
-            w, top = wl.weights, wl.top_experts
-        m = wl.pad_multiple if wl.layout == W.PADDED else None
-        cap = wl.capacity if wl.layout == W.BINNED else None
-        r = oracle.route_prep(top, wl.E, pad_multiple=m)
-        y = oracle.gather(wl.x, r, wl.layout, cap)
-        oracle.scatter_combine(y, wl.dtype, r, wl.layout, cap, weights=w.reshape(-1))
-        oracle.wgrad(y, wl.grad, wl.dtype, r, wl.layout, cap)
+        oracle_step(wl, W)
         t_total += time.perf_counter() - t0
         reps += 1
         if t_total >= seconds or reps >= 50:
@@ -371,6 +381,46 @@ def cpu_baseline(wl, W, seconds, bytes_step):
     return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole step(s) of the same workload (seed 0), {per_step * 1e3:.1f} ms per step, "
                       f"1 thread; tokens/s {wl.T / per_step:.1f}",
+            "cpu_model": cpu_model()}
+
+
+def cpu_threads():
+    """Host threads for the all-cores oracle leg: the CPUs this process may
+    run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline_threads(wl, W, seconds, bytes_step, threads):
+    """The same oracle steps on ``threads`` host threads at once, each thread
+    running whole independent steps of the workload until ``seconds`` of wall
+    time have passed (a step under way then finishes). The oracle's C calls
+    release the interpreter lock, so the threads run on separate cores; the
+    figure is whole-job throughput: completed steps x step bytes / wall time."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    oracle.round_bf16(0.0)  # opens the oracle library once, before the threads start
+
+    t_start = time.perf_counter()
+    deadline = t_start + seconds
+
+    def worker(_):
+        done = 0
+        while True:
+            oracle_step(wl, W)
+            done += 1
+            if time.perf_counter() >= deadline:
+                return done
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        steps = sum(pool.map(worker, range(threads)))
+    wall = time.perf_counter() - t_start
+    return {"value": round(steps * bytes_step / wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} whole independent step(s) of the same workload (seed 0) on {threads} threads "
+                      f"in {wall:.1f} s; tokens/s {steps * wl.T / wall:.1f}",
             "cpu_model": cpu_model()}
 
 
@@ -533,10 +583,14 @@ def main():
     ceilings = copy_ceiling(torch, HipEvents(), stream) if not args.no_events else None
     if roofline and ceilings:
         roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / ceilings["copy"], 4)
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu:
         log("timing the CPU oracle")
         cpu = cpu_baseline(wl, W, args.cpu_seconds, bytes_step)
+        threads = args.cpu_threads or cpu_threads()
+        if threads > 1:
+            log(f"timing the CPU oracle on {threads} threads")
+            cpu_all = cpu_baseline_threads(wl, W, args.cpu_seconds, bytes_step, threads)
 
     dtype_name = W.DTYPE_NAMES[wl.dtype]
     line = {
@@ -556,6 +610,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "streaming_GBps": ceilings,
         "outside_step": extras,
         "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},
