@@ -3,7 +3,8 @@
 * the product package never imports or loads the oracle (it is test
   infrastructure), and the HIP sources include nothing of it;
 * a missing library fails loudly (no CPU fallback);
-* bench.py refuses more than one GPU with a message and exit status 2.
+* bench.py refuses more than one GPU with a message and exit status 2;
+* its one-thread and all-cores CPU-oracle legs report whole steps.
 """
 import os
 import re
@@ -46,3 +47,18 @@ def test_bench_refuses_several_gpus():
                          timeout=300)
     assert out.returncode == 2
     assert "one GPU" in out.stderr
+
+
+def test_bench_cpu_oracle_legs():
+    """The one-thread and all-cores oracle legs of bench.py on the 512-token
+    batch: both report whole steps, the threaded one with its thread count."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as W
+    wl = W.config(1, 0)
+    one = bench.cpu_baseline(wl, W, 0.2, 1000)
+    two = bench.cpu_baseline_threads(wl, W, 0.2, 1000, 2)
+    for leg, cores in ((one, 1), (two, 2)):
+        assert leg["kind"] == "oracle" and leg["unit"] == "GB/s"
+        assert leg["cores"] == cores and leg["value"] > 0
+    assert 1 <= bench.cpu_threads() <= 16
