@@ -186,26 +186,41 @@ int64_t pego_route_prep(const int32_t* top_experts, int64_t T, int32_t K, int32_
 }
 
 /*
- * Row of sorted position i in the expert tensor, per the Implementation
- * Pattern of [BIN] (binned) and [PAD] (padded):
- *   expert start = 0 for expert 0, else bins[expert-1]; offset = i - start;
- *   binned: kept only if offset < capacity, row = expert*capacity + offset;
- *   padded: row = padded start (0 or padded_bins[expert-1]) + offset.
- * Returns -1 for a dropped position, -2 for a malformed expert id.
+ * Rows of the sorted positions [0, n) in the expert tensor ([BIN] and [PAD]
+ * Implementation Pattern). Every expert owns one segment of rows: in the
+ * binned layout expert e's segment is the `capacity` rows from e*capacity;
+ * in the padded layout it starts where the previous expert's padded segment
+ * ends (padded_bins[e-1], or 0 for the first expert). The walk below goes
+ * through the experts in turn; for each it visits the sorted positions in
+ * order, and every position of that expert receives the next unused row of
+ * the segment. A binned segment that has run out of rows drops the position
+ * (row -1). Returns a malloc'd array of n entries (at least one), or NULL
+ * when a position names no expert in [0, E) or memory runs out.
  */
-static int64_t position_row(int64_t i, int32_t E, int32_t layout, int32_t capacity,
-                            const int32_t* bin_ids, const int32_t* bins,
-                            const int32_t* padded_bins) {
-    int32_t expert = bin_ids[i];
-    if (expert < 0 || expert >= E) return -2;
-    int64_t real_start = expert == 0 ? 0 : bins[expert - 1];
-    int64_t offset = i - real_start;
-    if (layout == PEGO_BINNED) {
-        if (offset < capacity) return (int64_t)expert * capacity + offset;
-        return -1;
+static int64_t* position_rows(int64_t n, int32_t E, int32_t layout, int32_t capacity,
+                              const int32_t* bin_ids, const int32_t* padded_bins) {
+    int64_t* row_of = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+    if (!row_of) return NULL;
+    for (int64_t i = 0; i < n; ++i) row_of[i] = -2; /* not handed a row yet */
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t segment_base;
+        if (layout == PEGO_BINNED) segment_base = (int64_t)e * capacity;
+        else segment_base = e == 0 ? 0 : padded_bins[e - 1];
+        int64_t handed_out = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            if (bin_ids[i] != e) continue;
+            if (layout == PEGO_BINNED && handed_out >= capacity) row_of[i] = -1; /* segment full */
+            else row_of[i] = segment_base + handed_out;
+            ++handed_out;
+        }
     }
-    int64_t padded_start = expert == 0 ? 0 : padded_bins[expert - 1];
-    return padded_start + offset;
+    for (int64_t i = 0; i < n; ++i) {
+        if (row_of[i] == -2) { /* bin_ids[i] is not an expert */
+            free(row_of);
+            return NULL;
+        }
+    }
+    return row_of;
 }
 
 static int64_t valid_count(const int32_t* bins, int32_t E, int64_t total) {
@@ -230,24 +245,25 @@ int pego_assignment_rows(int64_t T, int32_t K, int32_t E, int32_t layout, int32_
     int64_t total = T * (int64_t)K;
     for (int64_t a = 0; a < total; ++a) rows_out[a] = -1;
     int64_t n = valid_count(bins, E, total);
+    int64_t* row_of = position_rows(n, E, layout, capacity, bin_ids, padded_bins);
+    if (!row_of) return -1;
     for (int64_t i = 0; i < n; ++i) {
-        int64_t row = position_row(i, E, layout, capacity, bin_ids, bins, padded_bins);
-        if (row == -2) return -1;
         int32_t a = indices[i];
-        if (a < 0 || a >= total) return -1;
-        rows_out[a] = (int32_t)row;
+        if (a < 0 || a >= total) { free(row_of); return -1; }
+        rows_out[a] = (int32_t)row_of[i];
     }
+    free(row_of);
     return 0;
 }
 
 /*
  * Rows of every assignment id when each expert owns a caller-given window of
- * rows [row_base[e], row_limit[e]): the Implementation Pattern's row formula
- * of [BIN] (segment start e*C plus the offset inside the expert, dropped past
- * the segment's C rows) and of [PAD] (padded segment start plus offset), with
- * the segment start and end supplied per expert. Sorted position i of expert
- * e = bin_ids[i] has offset i - start(e); its row is row_base[e] + offset if
- * that is below row_limit[e], else the assignment is dropped (-1).
+ * rows [row_base[e], row_limit[e]): the Implementation Pattern's segments of
+ * [BIN] and [PAD] with each expert's segment start and end supplied. The
+ * same walk as position_rows: experts in turn, each one's sorted positions
+ * in order, every position taking the next row of the expert's window from
+ * row_base[e] up; once a window's rows reach row_limit[e], the remaining
+ * assignments of that expert are dropped (-1).
  * (Used for one shard of a token-sharded batch: the windows then start where
  * the earlier shards' assignments of each expert end.)
  */
@@ -261,13 +277,16 @@ int pego_assignment_rows_windows(int64_t T, int32_t K, int32_t E, const int32_t*
     for (int64_t a = 0; a < total; ++a) rows_out[a] = -1;
     int64_t n = valid_count(bins, E, total);
     for (int64_t i = 0; i < n; ++i) {
-        int32_t expert = bin_ids[i];
-        if (expert < 0 || expert >= E) return -1;
-        int64_t start = expert == 0 ? 0 : bins[expert - 1];
-        int64_t row = (int64_t)row_base[expert] + (i - start);
-        int32_t a = indices[i];
-        if (a < 0 || a >= total) return -1;
-        rows_out[a] = row < row_limit[expert] ? (int32_t)row : -1;
+        if (bin_ids[i] < 0 || bin_ids[i] >= E) return -1;
+        if (indices[i] < 0 || indices[i] >= total) return -1;
+    }
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t next_row = row_base[e];
+        for (int64_t i = 0; i < n; ++i) {
+            if (bin_ids[i] != e) continue;
+            rows_out[indices[i]] = next_row < row_limit[e] ? (int32_t)next_row : -1;
+            ++next_row;
+        }
     }
     return 0;
 }
@@ -299,14 +318,16 @@ int pego_gather(const void* x, int64_t T, int64_t row_bytes, int32_t K, int32_t 
     if (!src) return -1;
     for (int64_t r = 0; r < R; ++r) src[r] = -1;
     int64_t n = valid_count(bins, E, total);
+    int64_t* row_of = position_rows(n, E, layout, capacity, bin_ids, padded_bins);
+    if (!row_of) { free(src); return -1; }
     for (int64_t i = 0; i < n; ++i) {
-        int64_t row = position_row(i, E, layout, capacity, bin_ids, bins, padded_bins);
-        if (row == -2) { free(src); return -1; }
+        int64_t row = row_of[i];
         if (row < 0 || row >= R) continue; /* dropped, or beyond the tensor */
         int64_t token = indices[i] / K;
-        if (indices[i] < 0 || token >= T) { free(src); return -1; }
+        if (indices[i] < 0 || token >= T) { free(src); free(row_of); return -1; }
         src[row] = token;
     }
+    free(row_of);
 
     const uint8_t* xb = (const uint8_t*)x;
     uint8_t* ob = (uint8_t*)out;
@@ -355,14 +376,16 @@ int pego_scatter_combine(const void* y, int32_t dtype, int64_t R, int64_t T, int
     if (!slot_src) return -1;
     for (int64_t a = 0; a < total; ++a) slot_src[a] = -1;
     int64_t n = valid_count(bins, E, total);
+    int64_t* row_of = position_rows(n, E, layout, capacity, bin_ids, padded_bins);
+    if (!row_of) { free(slot_src); return -1; }
     for (int64_t i = 0; i < n; ++i) {
-        int64_t row = position_row(i, E, layout, capacity, bin_ids, bins, padded_bins);
-        if (row == -2) { free(slot_src); return -1; }
+        int64_t row = row_of[i];
         if (row < 0) continue; /* beyond capacity: never read */
         int64_t a = indices[i];
-        if (a < 0 || a >= total || row >= R) { free(slot_src); return -1; }
+        if (a < 0 || a >= total || row >= R) { free(slot_src); free(row_of); return -1; }
         slot_src[a] = row;
     }
+    free(row_of);
 
     int64_t count = tokens ? ntok : T;
     for (int64_t j = 0; j < count; ++j) {
@@ -420,19 +443,21 @@ int pego_wgrad(const void* y, const void* grad, int32_t dtype, int64_t R, int64_
         if (a < 0 || a >= total) { free(pos_of); return -1; }
         pos_of[a] = i;
     }
+    int64_t* row_of = position_rows(n, E, layout, capacity, bin_ids, padded_bins);
+    if (!row_of) { free(pos_of); return -1; }
 
     int64_t count = tokens ? ntok : T;
     for (int64_t j = 0; j < count; ++j) {
         int64_t t = tokens ? tokens[j] : j;
-        if (t < 0 || t >= T) { free(pos_of); return -1; }
+        if (t < 0 || t >= T) { free(pos_of); free(row_of); return -1; }
         for (int32_t k = 0; k < K; ++k) {
             int64_t o = j * K + k;
             wgrad[o] = 0.0f;
             if (scale) scale[o] = 0.0;
             int64_t i = pos_of[t * K + k];
             if (i < 0) continue; /* no route */
-            int64_t row = position_row(i, E, layout, capacity, bin_ids, bins, padded_bins);
-            if (row == -2 || row >= R) { free(pos_of); return -1; }
+            int64_t row = row_of[i];
+            if (row >= R) { free(pos_of); free(row_of); return -1; }
             if (row < 0) continue; /* beyond capacity */
             double dot = 0.0, mag = 0.0;
             for (int64_t h = 0; h < H; ++h) {
@@ -445,6 +470,7 @@ int pego_wgrad(const void* y, const void* grad, int32_t dtype, int64_t R, int64_
         }
     }
     free(pos_of);
+    free(row_of);
     return 0;
 }
 
@@ -477,13 +503,15 @@ int pego_combine_backward_dy(const void* dout, int32_t dtype, int64_t T, int64_t
     if (!src) return -1;
     for (int64_t r = 0; r < R; ++r) src[r] = -1;
     int64_t n = valid_count(bins, E, total);
+    int64_t* row_of = position_rows(n, E, layout, capacity, bin_ids, padded_bins);
+    if (!row_of) { free(src); return -1; }
     for (int64_t i = 0; i < n; ++i) {
-        int64_t row = position_row(i, E, layout, capacity, bin_ids, bins, padded_bins);
-        if (row == -2) { free(src); return -1; }
+        int64_t row = row_of[i];
         if (row < 0 || row >= R) continue;
-        if (indices[i] < 0 || indices[i] >= total) { free(src); return -1; }
+        if (indices[i] < 0 || indices[i] >= total) { free(src); free(row_of); return -1; }
         src[row] = indices[i];
     }
+    free(row_of);
     int eb = dtype == PEGO_F32 ? 4 : 2;
     int64_t count = rows ? nrows : R;
     for (int64_t j = 0; j < count; ++j) {

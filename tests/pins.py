@@ -284,6 +284,34 @@ def _tiny_cases():
     return cases
 
 
+def pin_assignment_rows(o):
+    """The row of every assignment (the map every GPU test compares slot_row
+    with) against the per-expert enumeration, on the tiny routings, for both
+    layouts and several capacities and padding multiples; plus the counts
+    the pages fix: kept rows per expert = min(count, C) (binned) and the rows
+    of a padded segment start at the previous segment's rounded-up end."""
+    for top, _, E in _tiny_cases():
+        flat = top.reshape(-1)
+        counts = np.bincount(flat[flat >= 0], minlength=E)
+        for C in (1, 2, 3, 5, 64):
+            r = o.route_prep(top, E)
+            got = o.assignment_rows(r, W.BINNED, C)
+            want, _ = brute_rows(top, E, W.BINNED, capacity=C)
+            assert np.array_equal(got, want), f"binned rows C={C}"
+            kept = got[got >= 0]
+            assert len(np.unique(kept)) == len(kept)
+            assert np.array_equal(np.bincount(kept // C, minlength=E), np.minimum(counts, C))
+        for m in (1, 2, 3, 4, 8):
+            r = o.route_prep(top, E, pad_multiple=m)
+            got = o.assignment_rows(r, W.PADDED)
+            want, _ = brute_rows(top, E, W.PADDED, pad_multiple=m)
+            assert np.array_equal(got, want), f"padded rows m={m}"
+            starts = np.concatenate([[0], np.cumsum(-(-counts // m) * m)[:-1]])
+            for e in range(E):
+                mine = got[flat == e]
+                assert np.array_equal(np.sort(mine), starts[e] + np.arange(counts[e])), f"padded segment {e}"
+
+
 def pin_gather_numpy(o):
     """Gathers vs numpy fancy indexing into a zero tensor, with rows from the
     per-expert enumeration; also: zero rows are exactly zero, the number of
@@ -690,7 +718,7 @@ def pin_validate(o):
 
 
 ALL_PINS = [pin_bf16_rounding, pin_f16_rounding, pin_widening, pin_route_prep_numpy, pin_route_prep_exhaustive,
-            pin_route_prep_invariants, pin_golden, pin_gather_numpy, pin_gather_empty_batch,
+            pin_route_prep_invariants, pin_golden, pin_assignment_rows, pin_gather_numpy, pin_gather_empty_batch,
             pin_gather_bits_and_identity,
             pin_scatter_closed_form, pin_scatter_random_y, pin_wgrad_autograd, pin_wgrad_closed_form,
             pin_sampled_tokens, pin_combine_backward, pin_windows, pin_compaction, pin_router_selection,

@@ -25,11 +25,13 @@ MUTANTS = [
     ("bins_exclusive", "run += count;\n        bins[e] = (int32_t)run;",
      "bins[e] = (int32_t)run;\n        run += count;", 0),
     ("padded_round_down", "((count + pad_multiple - 1) / pad_multiple)", "(count / pad_multiple)", 0),
-    ("capacity_off_by_one", "if (offset < capacity)", "if (offset <= capacity)", 0),
-    ("binned_row_transposed", "(int64_t)expert * capacity + offset", "(int64_t)offset * capacity + expert", 0),
-    ("padded_start_from_bins", "padded_bins[expert - 1]", "bins[expert - 1]", 0),
-    ("real_start_wrong_bin", "int64_t real_start = expert == 0 ? 0 : bins[expert - 1];",
-     "int64_t real_start = expert == 0 ? 0 : bins[expert - 1] - (expert > 1);", 0),
+    ("capacity_off_by_one", "handed_out >= capacity", "handed_out > capacity", 0),
+    ("binned_segment_base", "segment_base = (int64_t)e * capacity;", "segment_base = (int64_t)e;", 0),
+    ("padded_start_inclusive", "segment_base = e == 0 ? 0 : padded_bins[e - 1];",
+     "segment_base = padded_bins[e];", 0),
+    ("walk_counter_off_by_one", "int64_t handed_out = 0;", "int64_t handed_out = e > 0;", 0),
+    ("walk_row_transposed", "else row_of[i] = segment_base + handed_out;",
+     "else row_of[i] = segment_base + (handed_out ^ 1);", 0),
     ("gather_token_div_2", "int64_t token = indices[i] / K;", "int64_t token = indices[i] / 2;", 0),
     ("scatter_weight_dropped", "double w = weights ? (double)weights[a] : 1.0;", "double w = 1.0;", 0),
     ("scatter_weight_of_k0", "double w = weights ? (double)weights[a] : 1.0;",
@@ -61,10 +63,8 @@ MUTANTS = [
     ("router_normalize_ignored", "(float)(normalize ? p[k] / sel : p[k])", "(float)p[k]", 0),
     ("router_selected_sum_first_only", "for (int32_t k = 0; k < K; ++k) sel += p[k];",
      "for (int32_t k = 0; k < 1; ++k) sel += p[k];", 0),
-    ("windows_limit_inclusive", "rows_out[a] = row < row_limit[expert] ? (int32_t)row : -1;",
-     "rows_out[a] = row <= row_limit[expert] ? (int32_t)row : -1;", 0),
-    ("windows_base_ignored", "int64_t row = (int64_t)row_base[expert] + (i - start);",
-     "int64_t row = (int64_t)row_base[0] + (i - start);", 0),
+    ("windows_limit_inclusive", "next_row < row_limit[e] ?", "next_row <= row_limit[e] ?", 0),
+    ("windows_base_ignored", "int64_t next_row = row_base[e];", "int64_t next_row = row_base[0];", 0),
     ("validate_no_duplicates", "if (seen[a]) flags |= FLAG_INDICES;", "(void)seen[a];", 0),
     ("validate_expected_off", "if (bins[e] <= i) ++expect;", "if (bins[e] < i) ++expect;", 0),
 ]
