@@ -14,8 +14,13 @@ Printed: one JSON line. ``value`` is the effective HBM bandwidth of the step,
 route_prep and compaction included); ``roofline`` is the dominant kernel's
 algorithmic bytes / its average duration (HIP events on its stream);
 ``cpu_baseline`` is the CPU oracle on the same workload, one thread;
-``cpu_baseline_all_cores`` runs independent whole oracle steps on every host
-thread available (at most 16) at once. ``backward`` times,
+``cpu_baseline_threads`` runs independent whole oracle steps on the host
+threads this process may use, at most 16 (one GPU's share of the host), with
+the host's CPU count and model recorded. ``kernels`` holds per-kernel
+durations inside the back-to-back steps; ``kernels_flushed`` the same
+kernels with 1 GiB written to scratch before each one (outside its event
+pair), so that none of its bytes come from L2 or the 256 MB Infinity Cache.
+``outside_step`` times,
 outside the step, the backward of the combine fused with wgrad on the same
 buffers (dy in the expert layout + the routing-weight gradient), and the
 router top-k gating (softmax, renormalised) of the workload's router scores,
@@ -76,12 +81,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, help="workload id 1-5 (default 2: Mixtral-8x7B-shaped)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="workload id 1-5 (default 5: Qwen2-MoE-57B-shaped, the largest one-GPU batch)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: enough for 2 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--cpu-threads", type=int, default=0,
-                    help="threads of the all-cores CPU-oracle leg (0: the host's CPUs, at most 16; 1: skip it)")
+                    help="threads of the multi-thread CPU-oracle leg (0: the CPUs this process may use, at most 16, "
+                         "one GPU's share of the host; 1: skip it)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-flushed per-op region")
+    ap.add_argument("--flush-bytes", type=int, default=1 << 30,
+                    help="bytes written before every op of the cache-flushed region (>= 1 GiB evicts L2 and MALL)")
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
     ap.add_argument("--no-router", action="store_true", help="skip timing the router gating")
@@ -292,9 +302,13 @@ class Step:
         if ev is not None:
             hip.record(ev[1], self.stream)
 
-    def run(self, events=None, hip=None):
+    def run(self, events=None, hip=None, before=None):
+        """One step; events: {op: (start, end)} recorded around each call;
+        before: called before each call (and before its start event)."""
         for name in self.order:
             fn, args = self.calls[name]
+            if before is not None:
+                before()
             if events is not None:
                 hip.record(events[name][0], self.stream)
             rc = fn(*args)
@@ -381,17 +395,27 @@ def cpu_baseline(wl, W, seconds, bytes_step):
     return {"value": round(bytes_step / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole step(s) of the same workload (seed 0), {per_step * 1e3:.1f} ms per step, "
                       f"1 thread; tokens/s {wl.T / per_step:.1f}",
-            "cpu_model": cpu_model()}
+            **host_record()}
+
+
+def allowed_cpus():
+    """CPUs this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
 def cpu_threads():
-    """Host threads for the all-cores oracle leg: the CPUs this process may
+    """Host threads for the multi-thread oracle leg: the CPUs this process may
     run on, at most 16 (one GPU's share of the host)."""
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    return max(1, min(allowed_cpus(), 16))
+
+
+def host_record():
+    """What the CPU figures ran on: the host's CPU count, the CPUs this
+    process may use, and the CPU model string."""
+    return {"host_cpus": os.cpu_count(), "allowed_cpus": allowed_cpus(), "cpu_model": cpu_model()}
 
 
 def cpu_baseline_threads(wl, W, seconds, bytes_step, threads):
@@ -421,7 +445,7 @@ def cpu_baseline_threads(wl, W, seconds, bytes_step, threads):
     return {"value": round(steps * bytes_step / wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} whole independent step(s) of the same workload (seed 0) on {threads} threads "
                       f"in {wall:.1f} s; tokens/s {steps * wl.T / wall:.1f}",
-            "cpu_model": cpu_model()}
+            "thread_cap": "16 threads: one GPU's share of the host", **host_record()}
 
 
 def cpu_model():
@@ -528,14 +552,17 @@ def main():
     # before and after every kernel. The event markers add a few microseconds
     # between kernels, which is why they stay out of region 1.
     use_ev = not args.no_events
-    kernels = {}
-    if use_ev:
+
+    def timed_steps(before=None):
+        """K steps with a HIP event pair around every kernel; returns the
+        per-kernel statistics."""
         hip = HipEvents()
         evs = [{n: (hip.create(), hip.create()) for n in names} for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
-            steps_obj[(args.warmup + i) % sets].run(evs[i], hip)
+            steps_obj[(args.warmup + i) % sets].run(evs[i], hip, before)
         torch.cuda.synchronize()
+        out = {}
         for n in names:
             ms = [hip.elapsed_ms(evs[i][n][0], evs[i][n][1]) for i in range(args.steps)]
             avg = sum(ms) / len(ms)
@@ -546,7 +573,27 @@ def main():
                 entry["bytes"] = ab[n]
                 entry["GBps"] = round(ab[n] / (avg / 1e3) / 1e9, 1)
                 entry["frac_peak"] = round(ab[n] / (avg / 1e3) / 1e9 / PEAK_GBS, 4)
-            kernels[n] = entry
+            out[n] = entry
+        return out
+
+    kernels = timed_steps() if use_ev else {}
+    # Timed region 2b (cache-flushed per-kernel durations): the same K steps
+    # with --flush-bytes (1 GiB) written to a scratch buffer on the stream
+    # before every kernel, outside its event pair: L2 and the 256 MB Infinity
+    # Cache then hold none of the kernel's inputs, even those the kernel before
+    # it has just written.
+    kernels_flushed = None
+    if use_ev and not args.no_flush:
+        flush_buf = torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev)
+        fills = [0]
+
+        def flush():
+            fills[0] += 1
+            with torch.cuda.stream(stream):
+                flush_buf.fill_(fills[0] & 255)
+
+        kernels_flushed = timed_steps(flush)
+        del flush_buf
     dominant = max(ab, key=lambda n: kernels[n]["avg_us"]) if use_ev else None
     roofline = None
     if dominant:
@@ -608,9 +655,11 @@ def main():
         "routed_tokens_per_s": round(wl.T / (ms_step / 1e3), 1),
         "step_bytes": bytes_step,
         "kernels": kernels,
+        "kernels_flushed": kernels_flushed,
+        "flush_bytes": None if kernels_flushed is None else args.flush_bytes,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "cpu_baseline_all_cores": cpu_all,
+        "cpu_baseline_threads": cpu_all,
         "streaming_GBps": ceilings,
         "outside_step": extras,
         "source_hash": {k: source_hash(k) for k in ("gather", "combine", "route_prep")},

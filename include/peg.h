@@ -227,7 +227,8 @@ peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int32_t lay
  * One pass over dout computes both:
  *   dy[row(a)] = w[a] * dout[a/K] for every kept assignment a (fp32 product,
  *                one rounding to dtype; raw bit copy when weights == NULL);
- *                every other row of [0, dy_rows) is zero (gap rows);
+ *                every other row of [0, dy_rows) is zero: the gap rows of
+ *                the layout and, when dy_rows > R, the rows [R, dy_rows);
  *   wgrad[a]   = <y[row(a)], dout[a/K]> as peg_wgrad.
  *   y [R, H], dout [T, H], dy [dy_rows, H], all of dtype; weights [T*K] f32
  *   or NULL; wgrad [T*K] f32, fully written. R = E*C (binned) or

@@ -320,6 +320,10 @@ def gather_padded(x, r, out=None, out_rows=None, err_flag=None, ws=None, use_slo
     x = _dev(x, "x")
     if r.padded_bins is None:
         raise ValueError("routing has no padded_bins")
+    if r.layout != PADDED and use_slot_row:
+        # its slot_row holds binned rows (e*C + offset), not padded ones
+        raise ValueError("routing was prepared for the binned layout: its slot_row does not address the padded "
+                         "tensor; route with pad_multiple only, or pass use_slot_row=False")
     if x.dim() != 2:
         raise ValueError("x must be [T, H]")
     _same_device(r, x, "x")

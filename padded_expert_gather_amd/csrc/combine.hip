@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
 // upstream gradient of the combine output, and while each of its vectors is
 // in registers it is also stored into the gradient of the expert tensor, dy,
 // at every kept row of the token - scaled by that route's weight (DY == 2)
-// or as raw bits (DY == 1). Blocks past token_blocks zero dy's gap rows.
+// or as raw bits (DY == 1). Blocks past token_blocks zero dy's gap rows and
+// its rows past the layout's (when dy has more).
 template <int DT, int VEC, int U, int WPT, int DY, int KR>
 __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const uint8_t* __restrict__ grad,
                                            float* __restrict__ wgrad, int64_t nch, int64_t slice, int64_t T,
@@ -180,7 +181,8 @@ __device__ __forceinline__ void wgrad_body(const uint8_t* __restrict__ y, const 
         const int64_t nz = (int64_t)gridDim.x - token_blocks;
         int64_t role_index;
         if (gap_role(blockIdx.x, gridDim.x, nz, &role_index)) {
-            zero_gap_rows<VEC, PEG_NT_STORE_DY_ZERO>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins, role_index, nz);
+            zero_gap_rows<VEC, PEG_NT_STORE_DY_ZERO>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins, role_index,
+                                                      nz, true);
             return;
         }
         tblock = role_index;

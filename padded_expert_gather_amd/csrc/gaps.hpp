@@ -69,23 +69,33 @@ inline int64_t gap_blocks(int64_t max_gap_rows, int64_t nch) {
 // Block zb of nz gap blocks zeroes its share of the gap rows of `out`
 // (out_rows rows of nch VEC-byte vectors). Binned: expert e's rows
 // [e*C + min(count, C), (e+1)*C); padded: [pstart(e) + count, padded_bins[e]).
-// Whole block must call it (contains barriers).
+// With zero_tail, the rows [R, out_rows) past the layout's R rows (E*C, or
+// padded_bins[E-1]) are one more gap. Whole block must call it (contains
+// barriers).
 template <int VEC, bool NT = PEG_NT_STORE_ZERO>
 __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t nch, int64_t out_rows,
                                               int32_t layout, int32_t E, int32_t capacity,
                                               const int32_t* __restrict__ bins,
-                                              const int32_t* __restrict__ padded_bins, int64_t zb, int64_t nz) {
+                                              const int32_t* __restrict__ padded_bins, int64_t zb, int64_t nz,
+                                              bool zero_tail = false) {
     using V = typename VecOf<VEC>::T;
-    // gap of expert e = rows [gstart[e], gstart[e] + glen[e]); gpre = exclusive
-    // prefix of glen. Rows at or past out_rows are never touched.
-    __shared__ int gpre[PEG_MAX_EXPERTS + 1];
-    __shared__ int gstart[PEG_MAX_EXPERTS];
+    // gap g = rows [gstart[g], gstart[g] + glen[g]) for g < NG (expert gaps,
+    // then the tail); gpre = exclusive prefix of glen. Rows at or past
+    // out_rows are never touched.
+    __shared__ int gpre[PEG_MAX_EXPERTS + 2];
+    __shared__ int gstart[PEG_MAX_EXPERTS + 1];
     __shared__ int scratch[kBlock / kWave];
+    const int NG = E + (zero_tail ? 1 : 0);
     int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kBlock) {
+    for (int e0 = 0; e0 < NG; e0 += kBlock) {
         const int e = e0 + threadIdx.x;
         int len = 0, start = 0;
-        if (e < E) {
+        if (e == E) {  // the tail past the layout's rows
+            const int64_t s = layout == PEG_BINNED ? (int64_t)E * capacity : (int64_t)padded_bins[E - 1];
+            const int64_t g = (s < 0 || s >= out_rows) ? 0 : out_rows - s;
+            len = (int)g;
+            start = (int)(g > 0 ? s : 0);
+        } else if (e < E) {
             int count = bins[e] - (e ? bins[e - 1] : 0);
             count = count < 0 ? 0 : count;
             int64_t s, g;
@@ -105,13 +115,13 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
         }
         int total;
         int pre = block_exclusive_scan<kBlock>(len, scratch, &total);
-        if (e < E) {
+        if (e < NG) {
             gpre[e] = carry + pre;
             gstart[e] = start;
         }
         carry += total;
     }
-    if (threadIdx.x == 0) gpre[E] = carry;
+    if (threadIdx.x == 0) gpre[NG] = carry;
     lds_barrier();
 
     const int64_t units = (int64_t)carry * nch;
@@ -138,8 +148,8 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
     const int64_t lo = units * zb / nz;
     const int64_t hi = units * (zb + 1) / nz;
     if (lo >= hi) return;
-    // first expert whose gap holds unit lo: last e with gpre[e] * nch <= lo
-    int a = 0, b = E - 1;
+    // first gap holding unit lo: last g with gpre[g] * nch <= lo
+    int a = 0, b = NG - 1;
     while (a < b) {
         const int mid = (a + b + 1) >> 1;
         if ((int64_t)gpre[mid] * nch <= lo) a = mid;
@@ -148,7 +158,7 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
     // walk this block's range one expert gap (a contiguous byte range) at a
     // time, kZeroUnroll stores in flight per thread
     int64_t u0 = lo;
-    for (int e = a; u0 < hi && e < E; ++e) {
+    for (int e = a; u0 < hi && e < NG; ++e) {
         const int64_t seg_end = (int64_t)gpre[e + 1] * nch < hi ? (int64_t)gpre[e + 1] * nch : hi;
         const int64_t shift = (int64_t)gstart[e] * nch - (int64_t)gpre[e] * nch;  // unit -> output vector
         for (int64_t u = u0 + threadIdx.x; u < seg_end; u += (int64_t)kBlock * kZeroUnroll) {

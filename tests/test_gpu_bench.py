@@ -3,7 +3,8 @@ batch (the small workload, so the run takes seconds).
 
 The line must be one JSON object with the metric, a positive throughput on one
 GPU, the workload named in ``config``, and a ``roofline`` object whose
-fraction is its achieved rate over MI355X's 8 TB/s; the CPU legs are skipped
+fraction is its achieved rate over MI355X's 8 TB/s, per-kernel durations in
+the back-to-back steps and with the caches flushed; the CPU legs are skipped
 here (tests/test_host.py covers them on the CPU).
 """
 import json
@@ -35,6 +36,8 @@ def test_bench_line():
     roof = rec["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["achieved"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
-    assert rec["cpu_baseline"] is None and rec["cpu_baseline_all_cores"] is None
+    assert rec["cpu_baseline"] is None and rec["cpu_baseline_threads"] is None
     for op in ("route_prep", "gather", "combine", "wgrad"):
         assert rec["kernels"][op]["avg_us"] > 0, op
+        assert rec["kernels_flushed"][op]["avg_us"] > 0, op
+    assert rec["flush_bytes"] >= 1 << 30

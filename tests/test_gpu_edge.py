@@ -329,3 +329,46 @@ def test_binding_refuses_bad_buffers():
         peg.validate_routing(rg, indices=rg.indices[:-1])
     torch.cuda.synchronize()
     assert int(peg.validate_routing(rg).item()) == 0                   # the routing itself is intact
+
+
+@pytest.mark.parametrize("layout", [W.BINNED, W.PADDED])
+def test_combine_backward_rows_past_layout(layout):
+    """dy with more rows than the layout's R: the kept rows and gaps as
+    usual, and every row of [R, dy_rows) zero (the buffer starts as a
+    sentinel); nothing is written past dy_rows."""
+    rng = np.random.default_rng(11 + layout)
+    T, K, E, H, C, m = 150, 2, 6, 72, 40, 8
+    top, w = W.random_routing(rng, T, K, E, skew=0.3, none_frac=0.1)
+    grad = W.normal(rng, (T, H), W.BF16)
+    cap = C if layout == W.BINNED else None
+    ro = oracle.route_prep(top, E, pad_multiple=m)
+    rg = peg.route_prep(to_dev(top), E, capacity=cap, pad_multiple=None if cap else m)
+    R = oracle.expert_rows(ro, layout, cap)
+    extra = 37
+    buf = torch.full((R + extra + 5, H), -7.0, dtype=torch.bfloat16, device=DEV)
+    yr = W.expert_tensor_rows(rng, R, H, W.BF16, used_rows=oracle.assignment_rows(ro, layout, cap)[
+        oracle.assignment_rows(ro, layout, cap) >= 0])
+    gg = to_dev(grad, W.BF16)
+    dyg, _ = peg.combine_backward(to_dev(yr, W.BF16), gg, rg, dy=buf[: R + extra], use_slot_row=True)
+    dyo = oracle.combine_backward_dy(grad, W.BF16, ro, layout, cap, weights=None)
+    bits_equal(to_host(dyg[:R]), dyo, "dy rows [0, R)")
+    assert int(buf[R: R + extra].view(torch.int16).count_nonzero().item()) == 0, "rows [R, dy_rows) not zero"
+    assert bool((buf[R + extra:] == -7.0).all()), "a row past dy_rows was written"
+
+
+def test_gather_padded_refuses_binned_routing():
+    """A routing prepared for the binned layout (capacity and pad_multiple
+    both given) carries padded_bins, but its slot_row holds binned rows:
+    gather_padded refuses it, and with use_slot_row=False rebuilds the
+    padded map and matches the oracle's padded gather."""
+    rng = np.random.default_rng(12)
+    T, K, E, H, C, m = 90, 2, 5, 48, 12, 8
+    top, _ = W.random_routing(rng, T, K, E, skew=0.5)
+    x = W.normal(rng, (T, H), W.BF16)
+    rg = peg.route_prep(to_dev(top), E, capacity=C, pad_multiple=m)
+    xg = to_dev(x, W.BF16)
+    with pytest.raises(ValueError):
+        peg.gather_padded(xg, rg)
+    ro = oracle.route_prep(top, E, pad_multiple=m)
+    bits_equal(to_host(peg.gather_padded(xg, rg, use_slot_row=False)), oracle.gather(x, ro, W.PADDED),
+               "padded gather of a binned routing, map rebuilt")

@@ -50,8 +50,9 @@ def test_bench_refuses_several_gpus():
 
 
 def test_bench_cpu_oracle_legs():
-    """The one-thread and all-cores oracle legs of bench.py on the 512-token
-    batch: both report whole steps, the threaded one with its thread count."""
+    """The one-thread and multi-thread oracle legs of bench.py on the
+    512-token batch: both report whole steps, the threaded one with its thread
+    count, and both the host's CPU count, the CPUs allowed and the model."""
     sys.path.insert(0, ROOT)
     import bench
     import workloads as W
@@ -61,4 +62,7 @@ def test_bench_cpu_oracle_legs():
     for leg, cores in ((one, 1), (two, 2)):
         assert leg["kind"] == "oracle" and leg["unit"] == "GB/s"
         assert leg["cores"] == cores and leg["value"] > 0
+        assert leg["host_cpus"] >= 1 and 1 <= leg["allowed_cpus"] <= leg["host_cpus"]
+        assert "cpu_model" in leg
+    assert "16" in two["thread_cap"]
     assert 1 <= bench.cpu_threads() <= 16
