@@ -90,7 +90,7 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
     for (int e0 = 0; e0 < NG; e0 += kBlock) {
         const int e = e0 + threadIdx.x;
         int len = 0, start = 0;
-        if (e == E) {  // the tail past the layout's rows
+        if (zero_tail && e == E) {  // the tail past the layout's rows
             const int64_t s = layout == PEG_BINNED ? (int64_t)E * capacity : (int64_t)padded_bins[E - 1];
             const int64_t g = (s < 0 || s >= out_rows) ? 0 : out_rows - s;
             len = (int)g;
