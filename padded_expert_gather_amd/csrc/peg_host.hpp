@@ -190,7 +190,7 @@ inline peg_status launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
 // Rebuilds the assignment -> row map from the sorted routing arrays into the
 // workspace (internal; shared by the gathers, the combine and wgrad).
 // Placement of the routing preparation from per-tile expert counts
-// (counts[e * ntiles + tile], tiles of kBlock * items ids, items one of
+// (counts[tile * E + e], tiles of kBlock * items ids, items one of
 // 1, 2, 4, 8, 16): writes indices, bin_ids, tokens_per_expert, bins,
 // padded_bins (if non-NULL) and slot_row (if non-NULL). Defined in
 // route_prep.hip.

@@ -10,10 +10,12 @@
 //
 // Ranking inside a 64-id chunk is a wave64 "multisplit": ballots over the bits
 // of the expert id give every lane the mask of lanes holding the same expert;
-// its rank is the popcount of that mask below the lane. Per-(chunk, expert)
-// counts are then scanned over chunks in LDS, which keeps ascending
-// assignment id inside every expert (a stable sort). No global atomics; the
-// result is deterministic.
+// its rank is the popcount of that mask below the lane. Every wave owns a
+// contiguous run of ids and walks its chunks in order, keeping per-expert
+// running counts in LDS; a scan over the waves per expert then gives each
+// wave's base. Positions therefore follow ascending assignment id inside
+// every expert (a stable sort). No global atomics; the result is
+// deterministic.
 //
 // Paths:
 //   small: T*K < 8192 and its count table fits in LDS -> one 1024-thread
@@ -42,41 +44,43 @@ __device__ __forceinline__ uint64_t same_expert_mask(int v, bool valid, int nbit
     return valid ? same : 0;
 }
 
-// In-place exclusive scan over the nch chunks of every expert column of the
-// LDS table cnt[nch][E]; tot[e] (optional) receives each expert's total.
-// Few experts: one wave per expert, a wave64 scan per 64 chunks. Many
-// experts: one thread per expert walks its column (conflict-free: adjacent
-// threads read adjacent words). Must be called by the whole block; ends
-// with a barrier.
-template <int NT>
-__device__ __forceinline__ void scan_chunks(int* cnt, int nch, int E, int* tot) {
-    constexpr int NW = NT / kWave;
-    if (E <= 16 * NW) {
-        const int lane = lane_id();
-        const int w = threadIdx.x / kWave;
-        for (int e = w; e < E; e += NW) {
-            int carry = 0;
-            for (int c0 = 0; c0 < nch; c0 += kWave) {
-                const int c = c0 + lane;
-                const int v = c < nch ? cnt[c * E + e] : 0;
-                const int inc = wave_inclusive_scan(v);
-                if (c < nch) cnt[c * E + e] = carry + inc - v;
-                carry += last_lane(inc);
-            }
-            if (tot && lane == 0) tot[e] = carry;
-        }
-    } else {
-        for (int e = threadIdx.x; e < E; e += NT) {
-            int run = 0;
-            for (int c = 0; c < nch; ++c) {
-                const int v = cnt[c * E + e];
-                cnt[c * E + e] = run;
-                run += v;
-            }
-            if (tot) tot[e] = run;
-        }
+// Ranks of a wave's ITEMS chunks of 64 ids, the ids in order (chunk j, lane
+// l): rank[j] = lanes below this one with the same expert in chunk j;
+// pre[j] = ids of the same expert in the wave's earlier chunks, read from the
+// wave's running counts wcnt[E] in LDS (all lanes read, then the first lane
+// of each expert adds the chunk's count; a wave's LDS operations complete in
+// order, so the next chunk reads the updated counts). wcnt ends holding the
+// wave's totals. Invalid ids (outside [0, E)) become -1 and are not counted.
+template <int ITEMS>
+__device__ __forceinline__ void wave_ranks(int (&v)[ITEMS], int E, int nbits, int* wcnt, int (&rank)[ITEMS],
+                                           int (&pre)[ITEMS]) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const bool valid = (unsigned)v[j] < (unsigned)E;
+        const uint64_t same = same_expert_mask(v[j], valid, nbits, E);
+        rank[j] = rank_below(same);
+        pre[j] = valid ? wcnt[v[j]] : 0;
+        if (valid && rank[j] == 0) wcnt[v[j]] = pre[j] + __popcll(same);
+        if (!valid) v[j] = -1;
     }
-    lds_barrier();
+}
+
+// Exclusive scan over the NW waves of each expert's count, in place in
+// wcnt[NW][E] (each entry becomes the ids of that expert in the earlier
+// waves); tot[e] (optional) receives the expert's total. One thread per
+// expert. Call from the whole block after a barrier; no barrier inside.
+template <int NW, int NT>
+__device__ __forceinline__ void scan_waves(int* wcnt, int E, int* tot) {
+    for (int e = threadIdx.x; e < E; e += NT) {
+        int run = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const int c = wcnt[ww * E + e];
+            wcnt[ww * E + e] = run;
+            run += c;
+        }
+        if (tot) tot[e] = run;
+    }
 }
 
 // Row of sorted position pos of expert e ([BIN]/[PAD] Implementation Pattern).
@@ -148,48 +152,43 @@ __global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
     int32_t capacity, int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
     int32_t* __restrict__ tokens_per_expert, int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
     int32_t* __restrict__ slot_row) {
-    constexpr int NCH = ITEMS * kSmallWaves;
     extern __shared__ int lds[];
-    int* cnt = lds;                 // [NCH][E]
-    int* start = cnt + NCH * E;     // [E] first sorted position of each expert
-    int* pstart = start + E;        // [E] first padded row of each expert
-    int* tot = pstart + E;          // [E] count of each expert
-    int* sidx = tot + E;            // [total] assignment id by sorted position (STAGE)
+    int* wcnt = lds;                       // [kSmallWaves][E] per-wave counts, then wave bases
+    int* start = wcnt + kSmallWaves * E;   // [E] first sorted position of each expert
+    int* pstart = start + E;               // [E] first padded row of each expert
+    int* tot = pstart + E;                 // [E] count of each expert
+    int* sidx = tot + E;                   // [total] assignment id by sorted position (STAGE)
     __shared__ int s_n;
 
-    // ids first: their loads overlap the table clearing
+    // wave w owns the ids [w * 64 * ITEMS, (w + 1) * 64 * ITEMS); their loads
+    // overlap the clearing of the counts
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t wbase = (int64_t)w * (kWave * ITEMS) + lane_id();
     int v[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int64_t a = (int64_t)j * kSmallThreads + threadIdx.x;
+        const int64_t a = wbase + j * kWave;
         v[j] = a < total ? top[a] : -1;
     }
-    for (int i = threadIdx.x; i < NCH * E; i += kSmallThreads) cnt[i] = 0;
+    for (int i = threadIdx.x; i < kSmallWaves * E; i += kSmallThreads) wcnt[i] = 0;
     lds_barrier();
 
-    const int w = threadIdx.x / kWave;
-    int rank[ITEMS];
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const bool valid = (unsigned)v[j] < (unsigned)E;
-        const uint64_t same = same_expert_mask(v[j], valid, nbits, E);
-        rank[j] = rank_below(same);
-        if (valid && rank[j] == 0) cnt[(j * kSmallWaves + w) * E + v[j]] = __popcll(same);
-        if (!valid) v[j] = -1;
-    }
+    int rank[ITEMS], pre[ITEMS];
+    wave_ranks<ITEMS>(v, E, nbits, wcnt + w * E, rank, pre);
     lds_barrier();
-    scan_chunks<kSmallThreads>(cnt, NCH, E, tot);  // ends with a barrier
+    scan_waves<kSmallWaves, kSmallThreads>(wcnt, E, tot);
+    lds_barrier();
     if (w == 0) wave0_bins(tot, E, pad_multiple, start, pstart, bins, padded_bins, tokens_per_expert, &s_n);
     lds_barrier();
 
     const int n = s_n;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int64_t a = (int64_t)j * kSmallThreads + threadIdx.x;
+        const int64_t a = wbase + j * kWave;
         if (a >= total) continue;
         const int e = v[j];
         if (e >= 0) {
-            const int pos = start[e] + cnt[(j * kSmallWaves + w) * E + e] + rank[j];
+            const int pos = start[e] + wcnt[w * E + e] + pre[j] + rank[j];
             if constexpr (STAGE) {
                 sidx[pos] = (int)a;
             } else {
@@ -228,6 +227,15 @@ __global__ __launch_bounds__(kSmallThreads) void prep_small_kernel(
 // Tiled path.
 // ---------------------------------------------------------------------------
 
+// The expert x tile count table is tile-major: counts[tile * E + e] (a
+// tile's counts are one contiguous run, written and read coalesced).
+// table_at(k) is the slot of entry k in expert-major order (k = e * ntiles
+// + tile), the order in which the sorted positions run.
+__device__ __forceinline__ int64_t table_at(int64_t k, int64_t ntiles, int32_t E) {
+    const int64_t e = k / ntiles;
+    return (k - e * ntiles) * E + e;
+}
+
 template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void tile_hist_kernel(const int32_t* __restrict__ top, int64_t total,
                                                            int32_t E, int64_t ntiles,
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void tile_hist_kernel(const int32_t* __rest
     for (int j = 0; j < ITEMS; ++j)
         if ((unsigned)v[j] < (unsigned)E) atomicAdd(&hist[v[j]], 1);
     lds_barrier();
-    for (int e = threadIdx.x; e < E; e += kBlock) counts[(int64_t)e * ntiles + blockIdx.x] = hist[e];
+    for (int e = threadIdx.x; e < E; e += kBlock) counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
 constexpr int kScanThreads = 1024;
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
         int s = 0;
 #pragma unroll
         for (int i = 0; i < kScanPer; ++i) {
-            v[i] = (my + i < L) ? counts[my + i] : 0;
+            v[i] = (my + i < L) ? counts[table_at(my + i, ntiles, E)] : 0;
             s += v[i];
         }
         int total;
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
 #pragma unroll
         for (int i = 0; i < kScanPer; ++i) {
             if (my + i < L) {
-                counts[my + i] = run;  // first sorted position of (expert, tile)
+                counts[table_at(my + i, ntiles, E)] = run;  // first sorted position of (expert, tile)
                 run += v[i];
             }
         }
@@ -286,8 +294,8 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
     const int e = threadIdx.x;
     int end_e = 0, end_prev = 0;
     if (e < E && ntiles > 0) {
-        end_e = (e + 1 < E) ? counts[(int64_t)(e + 1) * ntiles] : carry;
-        end_prev = e > 0 ? counts[(int64_t)e * ntiles] : 0;
+        end_e = (e + 1 < E) ? counts[e + 1] : carry;  // (tile 0, expert e + 1)
+        end_prev = e > 0 ? counts[e] : 0;
     }
     const int count = end_e - end_prev;
     if (e < E) {
@@ -302,12 +310,6 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
     }
 }
 
-// Table entries each placement thread loads at once while summing the
-// histogram table (4: T8192 K8 E256 16.8 us against 17.8 with one at a time;
-// 8 and 16 are no better).
-#ifndef PEG_SUM_BATCH
-#define PEG_SUM_BATCH 4
-#endif
 
 // Placement of one tile. With bases_ready (after tile_scan_kernel), `counts`
 // holds the first sorted position of every (expert, tile) and bins /
@@ -315,77 +317,77 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
 // every block derives its own bases from them (the whole table is small:
 // at most kMergedMaxTable ints); block 0 also writes tokens_per_expert,
 // bins and padded_bins.
-template <int ITEMS>
+// SB: table loads each placement thread keeps in flight while summing the
+// table (1, 4 or 32: about the tiles one thread sums).
+template <int ITEMS, int SB>
 __global__ __launch_bounds__(kBlock) void tile_place_kernel(
     const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, const int32_t* __restrict__ counts,
     int64_t ntiles, int32_t bases_ready, int32_t pad_multiple, int32_t layout, int32_t capacity,
     int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids, int32_t* __restrict__ tokens_per_expert,
     int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins, int32_t* __restrict__ slot_row) {
     constexpr int NW = kBlock / kWave;
-    constexpr int NCH = ITEMS * NW;  // 64-id chunks per tile
     extern __shared__ int lds[];
-    int* cnt = lds;              // [NCH][E]
-    int* tbase = cnt + NCH * E;  // [E] first sorted position of (e, this tile)
-    int* start = tbase + E;      // [E] first sorted position of e
-    int* pstart = start + E;     // [E] first padded row of e
+    int* wcnt = lds;              // [NW][E] per-wave counts of this tile, then each wave's base
+    int* tbase = wcnt + NW * E;   // [E] first sorted position of (e, this tile)
+    int* start = tbase + E;       // [E] first sorted position of e
+    int* pstart = start + E;      // [E] first padded row of e
     __shared__ int scratch[NW];
     __shared__ int s_n;
 
-    const int64_t base = (int64_t)blockIdx.x * (kBlock * ITEMS);
+    // wave w owns the tile's ids [w * 64 * ITEMS, (w + 1) * 64 * ITEMS)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t wbase = (int64_t)blockIdx.x * (kBlock * ITEMS) + (int64_t)w * (kWave * ITEMS) + lane_id();
     int v[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int64_t a = base + j * kBlock + threadIdx.x;
+        const int64_t a = wbase + j * kWave;
         v[j] = a < total ? top[a] : -1;
     }
+    for (int i = threadIdx.x; i < NW * E; i += kBlock) wcnt[i] = 0;
     if (bases_ready) {
         for (int e = threadIdx.x; e < E; e += kBlock) {
             start[e] = e ? bins[e - 1] : 0;
-            tbase[e] = counts[(int64_t)e * ntiles + blockIdx.x];
+            tbase[e] = counts[(int64_t)blockIdx.x * E + e];
             pstart[e] = (padded_bins && e) ? padded_bins[e - 1] : 0;
         }
         if (threadIdx.x == 0) s_n = bins[E - 1];
     } else {
         // each expert's total and this tile's offset inside it: the whole
-        // (experts x tiles) table (expert-major) is summed by all threads at
-        // once, each over its own contiguous segment, in registers, with one
-        // LDS atomic per expert the segment touches (pstart = totals, tbase =
-        // offsets); then scans over the experts give the starts
+        // expert x tile table is summed by all threads at once, in
+        // registers, with one LDS atomic per (expert, thread group)
+        // (pstart = totals, tbase = offsets); then scans over the experts
+        // give the starts
         for (int e = threadIdx.x; e < E; e += kBlock) {
             tbase[e] = 0;
             pstart[e] = 0;
         }
         lds_barrier();
         {
-            const int64_t table = ntiles * (int64_t)E;
-            const int64_t seg = (table + kBlock - 1) / kBlock;
-            const int64_t i0 = (int64_t)threadIdx.x * seg;
-            const int64_t i1 = i0 + seg < table ? i0 + seg : table;
-            if (i0 < i1) {
-                int e = (int)(i0 / ntiles);
-                int64_t t = i0 - (int64_t)e * ntiles;
-                int run = 0, run_before = 0;
-                // kSumBatch independent loads in flight, then the walk in registers
-                constexpr int kSumBatch = PEG_SUM_BATCH;
-                for (int64_t ib = i0; ib < i1; ib += kSumBatch) {
-                    int cb[kSumBatch];
+            // threads in groups of min(E, kBlock): thread e of group g sums
+            // expert e over the tiles g, g + groups, ... (SB loads in flight
+            // at a time; each load instruction of a wave reads consecutive
+            // experts of one tile: contiguous bytes)
+            const int eslots = E <= kBlock ? E : kBlock;
+            const int groups = kBlock / eslots;
+            const int g = threadIdx.x / eslots;
+            if (g < groups) {
+                for (int e = threadIdx.x - g * eslots; e < E; e += eslots) {
+                    int run = 0, run_before = 0;
+                    for (int64_t t0 = g; t0 < ntiles; t0 += (int64_t)groups * SB) {
+                        int cb[SB];
 #pragma unroll
-                    for (int q = 0; q < kSumBatch; ++q) cb[q] = ib + q < i1 ? counts[ib + q] : 0;
+                        for (int q = 0; q < SB; ++q) {
+                            const int64_t t = t0 + (int64_t)q * groups;
+                            cb[q] = t < ntiles ? counts[t * E + e] : 0;
+                        }
 #pragma unroll
-                    for (int q = 0; q < kSumBatch; ++q) {
-                        const int64_t i = ib + q;
-                        if (i >= i1) break;
-                        const int c = cb[q];
-                        run += c;
-                        run_before += t < (int64_t)blockIdx.x ? c : 0;
-                        if (++t == ntiles || i + 1 == i1) {  // end of this expert's row, or of the segment
-                            if (run) atomicAdd(&pstart[e], run);
-                            if (run_before) atomicAdd(&tbase[e], run_before);
-                            run = run_before = 0;
-                            t = 0;
-                            ++e;
+                        for (int q = 0; q < SB; ++q) {
+                            run += cb[q];
+                            run_before += t0 + (int64_t)q * groups < (int64_t)blockIdx.x ? cb[q] : 0;
                         }
                     }
+                    if (run) atomicAdd(&pstart[e], run);
+                    if (run_before) atomicAdd(&tbase[e], run_before);
                 }
             }
         }
@@ -418,30 +420,22 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
         }
         if (threadIdx.x == 0) s_n = carry;
     }
-    for (int i = threadIdx.x; i < NCH * E; i += kBlock) cnt[i] = 0;
-    lds_barrier();
+    lds_barrier();  // the cleared counts and the bases above, before the ranks and scans below
 
-    const int w = threadIdx.x / kWave;
-    int rank[ITEMS];
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const bool valid = (unsigned)v[j] < (unsigned)E;
-        const uint64_t same = same_expert_mask(v[j], valid, nbits, E);
-        rank[j] = rank_below(same);
-        if (valid && rank[j] == 0) cnt[(j * NW + w) * E + v[j]] = __popcll(same);
-        if (!valid) v[j] = -1;
-    }
+    int rank[ITEMS], pre[ITEMS];
+    wave_ranks<ITEMS>(v, E, nbits, wcnt + w * E, rank, pre);
     lds_barrier();
-    scan_chunks<kBlock>(cnt, NCH, E, nullptr);
+    scan_waves<NW, kBlock>(wcnt, E, nullptr);
+    lds_barrier();
 
     const int n = s_n;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int64_t a = base + j * kBlock + threadIdx.x;
+        const int64_t a = wbase + j * kWave;
         if (a >= total) continue;
         const int e = v[j];
         if (e >= 0) {
-            const int pos = tbase[e] + cnt[(j * NW + w) * E + e] + rank[j];
+            const int pos = tbase[e] + wcnt[w * E + e] + pre[j] + rank[j];
             indices[pos] = (int32_t)a;
             bin_ids[pos] = e;
             if (slot_row) slot_row[a] = position_row(layout, e, capacity, pos - start[e], pstart[e]);
@@ -478,10 +472,17 @@ static peg_status place_tiles(const int32_t* top, int64_t total, int32_t E, int3
         PEG_CHECK(launch(tile_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E, pad_multiple, tpe,
                          bins, padded_bins));
     if (ntiles == 0) return PEG_OK;
-    const size_t lds = ((size_t)ITEMS * (kBlock / kWave) * E + 3 * (size_t)E) * sizeof(int);
-    return launch(tile_place_kernel<ITEMS>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,
-                  id_bits(E), counts, ntiles, merged ? 0 : 1, pad_multiple, layout, capacity, indices, bin_ids, tpe,
-                  bins, padded_bins, slot_row);
+    const size_t lds = ((size_t)(kBlock / kWave) * E + 3 * (size_t)E) * sizeof(int);
+    const int64_t groups = kBlock / (E <= kBlock ? E : kBlock);
+    const int64_t per = merged ? (ntiles + groups - 1) / groups : 1;  // tiles one thread sums
+#define PEG_PLACE_LAUNCH(SB)                                                                                    \
+    return launch(tile_place_kernel<ITEMS, SB>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,    \
+                  id_bits(E), counts, ntiles, merged ? 0 : 1, pad_multiple, layout, capacity, indices, bin_ids, tpe, \
+                  bins, padded_bins, slot_row)
+    if (per <= 1) PEG_PLACE_LAUNCH(1);
+    if (per <= 4) PEG_PLACE_LAUNCH(4);
+    PEG_PLACE_LAUNCH(32);
+#undef PEG_PLACE_LAUNCH
 }
 
 template <int ITEMS>
@@ -500,7 +501,7 @@ template <int ITEMS>
 static peg_status prep_small(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
                              int32_t pad_multiple, int32_t* indices, int32_t* bin_ids, int32_t* tpe, int32_t* bins,
                              int32_t* padded_bins, int32_t* slot_row, hipStream_t s) {
-    const size_t base = ((size_t)ITEMS * kSmallWaves * E + 3 * (size_t)E) * sizeof(int);
+    const size_t base = ((size_t)kSmallWaves * E + 3 * (size_t)E) * sizeof(int);
     const size_t staged = base + (size_t)total * sizeof(int);
     if (staged <= kSmallMaxLds)
         return launch(prep_small_kernel<ITEMS, true>, dim3(1), dim3(kSmallThreads), staged, s, top, total, E,
@@ -514,7 +515,7 @@ static int small_items(int64_t total, int32_t E) {
     if (total > kSmallMaxIds) return 0;
     int items = 1;
     while ((int64_t)items * kSmallThreads < total) items <<= 1;
-    if ((size_t)items * kSmallWaves * E * sizeof(int) > kSmallMaxTable) return 0;
+    if ((size_t)kSmallWaves * E * sizeof(int) > kSmallMaxTable) return 0;
     return items;
 }
 

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const void* __restr
 // the assignment ids [b * tile, (b + 1) * tile) and gates every token that
 // has an id there (a token that straddles two tiles is gated by both blocks,
 // identically; the block holding its first id writes its outputs). The
-// block's expert histogram of its ids goes to counts[e * ntiles + b], the
+// block's expert histogram of its ids goes to counts[b * E + e], the
 // table the placement pass reads.
 constexpr int kHistThreads = 1024;  // gating lanes of a tile: 128 tokens per pass at 8 lanes per token
 
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kHistThreads) void router_hist_kernel(const void* _
         }
     }
     lds_barrier();
-    for (int e = threadIdx.x; e < E; e += kHistThreads) counts[(int64_t)e * ntiles + blockIdx.x] = hist[e];
+    for (int e = threadIdx.x; e < E; e += kHistThreads) counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
 // Launch arguments of both gating kernels.
