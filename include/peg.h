@@ -54,6 +54,8 @@ typedef int32_t peg_status;
 #define PEG_ERR_WORKSPACE 4     /* ws is NULL or ws_bytes is too small */
 #define PEG_ERR_LAUNCH 5        /* the HIP runtime rejected a launch */
 #define PEG_ERR_ALIGNMENT 6     /* a pointer is not aligned to its element */
+#define PEG_ERR_SCRATCH_LIMIT 7 /* the sizes need more than the static scratch of an
+                                   allocation-free entry point */
 
 /* Element types. Gathers move bits and accept any of them. */
 #define PEG_F32 0
@@ -127,6 +129,35 @@ peg_status peg_route_prep(const int32_t* top_experts, int64_t T, int32_t K, int3
                           int32_t* indices, int32_t* bin_ids, int32_t* tokens_per_expert,
                           int32_t* bins, int32_t* padded_bins, int32_t* slot_row,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the library's own device scratch behind peg_route_prep_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define PEG_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * peg_route_prep_noalloc - peg_route_prep for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and outputs, bit for
+ * bit, without the workspace. It allocates nothing and frees nothing; its
+ * scratch (the per-tile expert counts of batches of 8192 assignments and
+ * more) is a static array of PEG_NOALLOC_SCRATCH_BYTES in the library's
+ * device memory, one per GPU.
+ *   Limit: the count table takes ceil(T*K / tile) * E * 4 bytes, the tile
+ *   being 2048 assignments for E <= 256, 1024 for E <= 512, 512 above (and
+ *   smaller for batches under 64 tiles); sizes beyond the scratch return
+ *   PEG_ERR_SCRATCH_LIMIT and enqueue nothing. The scratch holds up to
+ *   2,097,152 assignments at E = 256 and 131,072 at E = 1024.
+ *   The scratch needs no clearing (every entry a call reads, it writes
+ *   first). Every call on one GPU uses that GPU's one array: calls that may
+ *   overlap on one GPU (other streams, other host threads) race and must be
+ *   serialised by the caller. The stream must belong to the calling thread's
+ *   current device (the array of that device is used).
+ * Errors: those of peg_route_prep (without WORKSPACE), SCRATCH_LIMIT.
+ */
+peg_status peg_route_prep_noalloc(const int32_t* top_experts, int64_t T, int32_t K, int32_t E,
+                                  int32_t layout, int32_t capacity, int32_t pad_multiple,
+                                  int32_t* indices, int32_t* bin_ids, int32_t* tokens_per_expert,
+                                  int32_t* bins, int32_t* padded_bins, int32_t* slot_row, void* stream);
 
 /*
  * peg_gather_binned - binned dispatch into [E, C, H].

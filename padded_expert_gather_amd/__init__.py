@@ -7,7 +7,7 @@ only. There is no CPU fallback: on a machine without the GPU library or
 without a GPU the calls raise.
 
 Functions (same names as the C entry points without the ``peg_`` prefix):
-  route_prep, gather_binned, gather_padded, scatter_combine, wgrad,
+  route_prep, route_prep_noalloc, gather_binned, gather_padded, scatter_combine, wgrad,
   combine_backward, router_topk, route_prep_logits, route_prep_windows,
   gather_rows, routing_map_compact,
   routing_map_compact_backward, validate_routing.
@@ -58,6 +58,8 @@ def _load():
         "peg_workspace_bytes": ([c_int64, c_int32, c_int32], c_size_t),
         "peg_route_prep": ([P, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, P, P, c_size_t,
                             P], st),
+        "peg_route_prep_noalloc": ([P, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, P, P],
+                                   st),
         "peg_gather_binned": ([P, c_int32, c_int64, c_int64, c_int32, c_int32, c_int32, P, P, P, P, P, P, c_size_t,
                                P], st),
         "peg_gather_padded": ([P, c_int32, c_int64, c_int64, c_int32, c_int32, P, P, P, P, P, P, c_int64, P, P,
@@ -93,7 +95,7 @@ def library():
 def _check(status, what):
     if status != 0:
         msg = _load().peg_status_string(status).decode()
-        exc = ValueError if status in (1, 2, 3, 4, 6) else PegError
+        exc = ValueError if status in (1, 2, 3, 4, 6, 7) else PegError
         raise exc(f"{what}: {msg} (status {status})")
 
 
@@ -185,6 +187,46 @@ def route_prep(top_experts, num_experts, capacity=None, pad_multiple=None, ws=No
                                     _ptr(slot_row), _ptr(ws), wsb, _stream(dev))
     _check(st, "route_prep")
     return Routing(T, K, E, layout, capacity, pad_multiple, indices, bin_ids, tpe, bins, padded, slot_row)
+
+
+def route_prep_noalloc(top_experts, num_experts, capacity=None, pad_multiple=None, out=None):
+    """route_prep through the allocation-free entry point (the library's own
+    static device scratch, no workspace). ``out`` may hold preallocated
+    output tensors (a Routing of the same sizes) so that nothing at all is
+    allocated; otherwise they are allocated here, before the call."""
+    top = _dev(top_experts, "top_experts", torch.int32)
+    if top.dim() != 2:
+        raise ValueError("top_experts must be [T, K]")
+    T, K = top.shape
+    E = int(num_experts)
+    if capacity is None and pad_multiple is None:
+        raise ValueError("give capacity (binned) or pad_multiple (padded)")
+    layout = BINNED if capacity is not None else PADDED
+    dev = top.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = Routing(T, K, E, layout, capacity, pad_multiple, torch.empty(T * K, **i32), torch.empty(T * K, **i32),
+                      torch.empty(E, **i32), torch.empty(E, **i32),
+                      torch.empty(E, **i32) if pad_multiple is not None else None, torch.empty(T * K, **i32))
+    else:
+        out.T, out.K, out.E, out.layout, out.capacity, out.pad_multiple = T, K, E, layout, capacity, pad_multiple
+    for name, t, n in (("indices", out.indices, T * K), ("bin_ids", out.bin_ids, T * K),
+                       ("tokens_per_expert", out.tokens_per_expert, E), ("bins", out.bins, E),
+                       ("slot_row", out.slot_row, T * K)):
+        _dev(t, name, torch.int32)
+        if t.numel() < n:
+            raise ValueError(f"{name} must hold {n} values")
+    if pad_multiple is not None:
+        if out.padded_bins is None or out.padded_bins.numel() < E:
+            raise ValueError("padded_bins must hold E values")
+    with torch.cuda.device(dev):
+        st = _load().peg_route_prep_noalloc(_ptr(top), T, K, E, layout, int(capacity or 0), int(pad_multiple or 0),
+                                            _ptr(out.indices), _ptr(out.bin_ids), _ptr(out.tokens_per_expert),
+                                            _ptr(out.bins), _ptr(out.padded_bins if pad_multiple is not None
+                                                                 else None),
+                                            _ptr(out.slot_row), _stream(dev))
+    _check(st, "route_prep_noalloc")
+    return out
 
 
 def route_prep_logits(logits, K, capacity=None, pad_multiple=None, gating=SOFTMAX, normalize=True, ws=None):

@@ -13,6 +13,7 @@ PEG_API const char* peg_status_string(peg_status s) {
         case PEG_ERR_WORKSPACE: return "workspace missing or too small";
         case PEG_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
         case PEG_ERR_ALIGNMENT: return "a buffer is not aligned to its element size";
+        case PEG_ERR_SCRATCH_LIMIT: return "the sizes need more than the library's static scratch";
         default: return "unknown status";
     }
 }

@@ -26,6 +26,9 @@
 //          table and derives its own bases (block 0 also writes the bins);
 //          when that table is large, a single-block scan launch in between
 //          computes the bases once.
+#include <atomic>
+#include <mutex>
+
 #include "peg_device.hpp"
 #include "peg_host.hpp"
 
@@ -519,6 +522,13 @@ static int small_items(int64_t total, int32_t E) {
     return items;
 }
 
+// Scratch bytes that prep_dispatch uses for these sizes: none on the
+// small path, the (experts x tiles) count table on the tiled path.
+static size_t prep_scratch_bytes(int64_t total, int32_t E) {
+    if (small_items(total, E)) return 0;
+    return (size_t)prep_tiles(total, E) * (size_t)E * sizeof(int32_t);
+}
+
 // Everything of peg_route_prep after its argument checks; counts: the
 // workspace.
 static peg_status prep_dispatch(const int32_t* top_experts, int64_t total, int32_t E, int32_t layout,
@@ -639,4 +649,62 @@ PEG_API peg_status peg_route_prep_windows(const int32_t* top_experts, int64_t T,
     if (total == 0) return PEG_OK;
     return launch(windows_kernel, dim3((unsigned)((total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, top_experts,
                   total, E, bins, row_base, row_limit, slot_row);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free routing preparation.
+// ---------------------------------------------------------------------------
+
+// The count table of peg_route_prep_noalloc lives in this array: device
+// memory of the library, one copy per GPU the library runs on, held until
+// the process ends. Host code never uses the array's name as an address (on
+// the host it names a stand-in): the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[PEG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (resolved on the first
+// call for that device).
+peg_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PEG_ERR_LAUNCH;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PEG_ERR_LAUNCH;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return PEG_OK;
+}
+}  // namespace
+
+PEG_API peg_status peg_route_prep_noalloc(const int32_t* top_experts, int64_t T, int32_t K, int32_t E,
+                                          int32_t layout, int32_t capacity, int32_t pad_multiple,
+                                          int32_t* indices, int32_t* bin_ids, int32_t* tokens_per_expert,
+                                          int32_t* bins, int32_t* padded_bins, int32_t* slot_row, void* stream) {
+    if (!layout_ok(layout)) return PEG_ERR_BAD_DTYPE;
+    if (T < 0 || K < 1 || E < 1 || E > PEG_MAX_EXPERTS) return PEG_ERR_BAD_SHAPE;
+    if (T > kMaxAssign / K) return PEG_ERR_BAD_SHAPE;
+    const int64_t total = T * (int64_t)K;
+    if (layout == PEG_BINNED && capacity < 1) return PEG_ERR_BAD_SHAPE;
+    if (layout == PEG_BINNED && (int64_t)E * capacity > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    const bool need_pad = padded_bins != nullptr || layout == PEG_PADDED;
+    if (need_pad && pad_multiple < 1) return PEG_ERR_BAD_SHAPE;
+    if (need_pad && total + (int64_t)E * (pad_multiple - 1) > kMaxAssign) return PEG_ERR_BAD_SHAPE;
+    if (!bins || (total > 0 && (!top_experts || !indices || !bin_ids))) return PEG_ERR_NULL_ARG;
+    if (layout == PEG_PADDED && !padded_bins) return PEG_ERR_NULL_ARG;
+    if (prep_scratch_bytes(total, E) > (size_t)PEG_NOALLOC_SCRATCH_BYTES) return PEG_ERR_SCRATCH_LIMIT;
+    void* counts = nullptr;
+    PEG_CHECK(scratch_address(&counts));
+    return prep_dispatch(top_experts, total, E, layout, capacity, pad_multiple, indices, bin_ids, tokens_per_expert,
+                         bins, padded_bins, slot_row, reinterpret_cast<int32_t*>(counts),
+                         reinterpret_cast<hipStream_t>(stream));
 }

@@ -34,6 +34,9 @@ int main(void) {
                           1 << 20, NULL) == PEG_ERR_BAD_SHAPE, "route_prep E = 0");
     expect(peg_route_prep(NULL, 4, 2, 4, PEG_BINNED, 2, 0, ifake, ifake, NULL, ifake, NULL, NULL, fake, 1 << 20,
                           NULL) == PEG_ERR_NULL_ARG, "route_prep NULL top_experts");
+    expect(peg_route_prep_noalloc(ifake, 131073, 1, 1024, PEG_BINNED, 200, 0, ifake, ifake, NULL, ifake, NULL, NULL,
+                                  NULL) == PEG_ERR_SCRATCH_LIMIT, "route_prep_noalloc past its scratch");
+    expect(PEG_NOALLOC_SCRATCH_BYTES == (1u << 20), "static scratch size");
     expect(peg_gather_binned(fake, 9, 4, 8, 2, 4, 2, ifake, ifake, ifake, ifake, fake, fake, 1 << 20, NULL) ==
                PEG_ERR_BAD_DTYPE, "gather_binned bad dtype");
     expect(peg_scatter_combine(fake, PEG_BF16, PEG_BINNED, 4, 8, 2, 4, 2, ifake, ifake, ifake, NULL, ifake, NULL,

@@ -15,7 +15,7 @@ import padded_expert_gather_amd as peg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "peg.h")
 
-OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, WORKSPACE, LAUNCH, ALIGNMENT = 0, 1, 2, 3, 4, 5, 6
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, WORKSPACE, LAUNCH, ALIGNMENT, SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def declared_symbols():
@@ -30,15 +30,15 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_status_and_workspace(lib):
     assert lib.peg_abi_version() >> 16 == 1
-    for s in range(7):
-        assert lib.peg_status_string(s)
+    for s in range(8):
+        assert lib.peg_status_string(s) != b"unknown status"
     assert lib.peg_status_string(99) == b"unknown status"
     assert lib.peg_workspace_bytes(-1, 2, 8) == 0
     assert lib.peg_workspace_bytes(10, 0, 8) == 0
@@ -81,6 +81,30 @@ def test_route_prep_checks(lib):
     assert call(layout=1, m=4, pb=None) == NULL_ARG    # padded layout needs padded_bins
     assert call(ws=None) == WORKSPACE
     assert call(wsb=8) == WORKSPACE
+
+
+def test_route_prep_noalloc_checks(lib):
+    """The allocation-free routing preparation: the checks of route_prep, and
+    sizes past its static scratch refused before any HIP call."""
+    f = lib.peg_route_prep_noalloc
+    base = dict(top=_p(FAKE), T=4, K=2, E=4, layout=0, C=2, m=0, idx=_p(FAKE), bid=_p(FAKE), tpe=None,
+                bins=_p(FAKE), pb=None, sr=None, s=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["top"], a["T"], a["K"], a["E"], a["layout"], a["C"], a["m"], a["idx"], a["bid"], a["tpe"],
+                 a["bins"], a["pb"], a["sr"], a["s"])
+
+    assert call(layout=7) == BAD_DTYPE
+    assert call(T=-1) == BAD_SHAPE
+    assert call(E=1025) == BAD_SHAPE
+    assert call(C=0) == BAD_SHAPE
+    assert call(top=None) == NULL_ARG
+    assert call(layout=1, m=4, pb=None) == NULL_ARG
+    # E = 1024 tiles hold 512 assignments: 131,073 of them need 257 tiles of
+    # 1024 counts (1,052,672 bytes), past the 1 MiB scratch
+    assert call(T=131073, K=1, E=1024, C=200) == SCRATCH_LIMIT
+    assert call(T=(1 << 20) + 256, K=8, E=64, C=200) == SCRATCH_LIMIT  # 4097 tiles of 2048 x 64
 
 
 def test_gather_checks(lib):
