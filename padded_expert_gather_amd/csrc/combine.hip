@@ -651,8 +651,14 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     const int64_t q = wave_slice(nch, sh.wpt);
     const int u = pass_vectors(q, sh.umax);
     const int64_t tb = token_blocks(T, sh.wpt);
-    if (!grid_fits(tb + gap_blocks(dy_rows, nch), kBlock)) return PEG_ERR_BAD_SHAPE;
-    const dim3 grid((unsigned)(tb + gap_blocks(dy_rows, nch)));
+    // a large binned dy gets its gap rows (and rows past E*C) from a
+    // fill-shaped launch of its own first; otherwise gap blocks follow the
+    // token blocks in one launch
+    const bool fill = dy_rows > 0 && use_gap_fill(layout, dy_rows, H * eb, E);
+    const int64_t nzb = fill ? 0 : gap_blocks(dy_rows, nch);
+    if (!grid_fits(tb + nzb, kBlock)) return PEG_ERR_BAD_SHAPE;
+    const dim3 grid((unsigned)(tb + nzb));
+    if (fill) PEG_CHECK(launch_gap_fill_vec(vec, (uint8_t*)dy, nch, dy_rows, E, capacity, bins, s));
     const WgradArgs a{(const uint8_t*)y, (const uint8_t*)dout, wgrad, nch, q, T, K, slot_row, ra, E, weights,
                       (uint8_t*)dy, dy_rows, layout, capacity, bins, tb, sh.wpt};
     if (weights) return wgrad_by_dtype<2>(dtype, vec, u, grid, s, a);

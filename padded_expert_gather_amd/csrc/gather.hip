@@ -15,9 +15,11 @@
 //   * the rows of a token come from the assignment -> row map (slot_row) by
 //     wave-uniform scalar loads, so the row loads issue at once, with no LDS
 //     staging or barrier in front of them;
-//   * in the same launch, trailing "gap" blocks write zeros into the unused
+//   * trailing "gap" blocks of the same launch write zeros into the unused
 //     capacity / padding rows only (each gap of an expert is one contiguous
-//     byte range), so no row is written twice and no memset pass is needed.
+//     byte range), so no row is written twice and no memset pass is needed;
+//     a large binned tensor gets its gap rows from a fill-shaped launch of
+//     their own just before (gap_fill_kernel).
 #include "gaps.hpp"
 #include "peg_device.hpp"
 #include "peg_host.hpp"
@@ -197,10 +199,15 @@ static peg_status gather_common(const void* x, int32_t dtype, int64_t T, int64_t
         slot_row = rebuilt;
     }
     const int64_t nch = row_bytes / vec;
-    const int64_t nz = gap_blocks(out_rows, nch);
+    // large binned tensors: the gap rows in a fill-shaped launch of their own
+    // first, then token blocks only; otherwise gap blocks after the token
+    // blocks of one launch
+    const bool fill = use_gap_fill(layout, out_rows, row_bytes, E);
+    const int64_t nz = fill ? 0 : gap_blocks(out_rows, nch);
     const int wpt = gather_wpt(nch, K);
     const int64_t tb = token_blocks(T, wpt);
     if (!grid_fits(tb + nz, kBlock)) return PEG_ERR_BAD_SHAPE;
+    if (fill) PEG_CHECK(launch_gap_fill_vec(vec, (uint8_t*)out, nch, out_rows, E, capacity, bins, s));
     const dim3 grid((unsigned)(tb + nz));
     const int64_t slice = wave_slice(nch, wpt);
     const int u = lanes_per_pass(slice);

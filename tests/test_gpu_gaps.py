@@ -174,3 +174,36 @@ def test_tensor_beyond_2gib():
         assert torch.equal(dv[rk[sl]], want_rows.view(torch.int16)), "backward dy kept rows"
     assert int(dv[gap].count_nonzero().item()) == 0, "backward dy gap rows"
     assert torch.equal(wgb, wgr), "fused wgrad == wgrad kernel"
+
+
+def test_large_binned_dy_rows_past_layout():
+    """The combine backward into a binned dy of more than 128 MB (its gap
+    rows then come from the fill-shaped launch) with more rows than E*C:
+    kept rows are w * dout, gap rows and the rows [E*C, dy_rows) are zero,
+    rows past dy_rows untouched; the fused wgrad equals the wgrad kernel."""
+    print("[gaps dy tail]", flush=True)
+    rng = np.random.default_rng(31)
+    T, K, E, H, C = 20000, 2, 8, 2048, 4096
+    extra = 1000
+    assert E * C * H * 2 >= 128 << 20
+    top, w = W.random_routing(rng, T, K, E, none_frac=0.05, skew=0.4)
+    dout = W.normal(rng, (T, H), W.BF16)
+    ro = oracle.route_prep(top, E)
+    rg = peg.route_prep(to_dev(top), E, capacity=C)
+    xg = to_dev(W.normal(rng, (T, H), W.BF16), W.BF16)
+    y = peg.gather_binned(xg, rg)
+    buf = _filled(E * C + extra + 64, H, W.BF16)
+    dg = to_dev(dout, W.BF16)
+    wg = to_dev(w.reshape(-1))
+    dy, wgb = peg.combine_backward(y, dg, rg, weights=wg, dy=buf[:E * C + extra])
+    rows = oracle.assignment_rows(ro, W.BINNED, C)
+    kept = np.flatnonzero(rows >= 0)
+    rk = torch.from_numpy(rows[kept].astype(np.int64)).to(DEV)
+    tk = torch.from_numpy(kept.astype(np.int64)).to(DEV)
+    want = (wg[tk].unsqueeze(1) * dg[tk // K].float()).to(torch.bfloat16)
+    assert torch.equal(dy[rk].view(torch.int16), want.view(torch.int16)), "kept rows of dy"
+    gap = torch.ones(E * C + extra, dtype=torch.bool, device=DEV)
+    gap[rk] = False
+    assert int(dy[gap].view(torch.int16).count_nonzero().item()) == 0, "gap or tail rows of dy not zero"
+    assert (to_host(buf[E * C + extra:]).view(np.uint8) == 0xFF).all(), "rows past dy_rows were written"
+    assert torch.equal(wgb, peg.wgrad(y, dg, rg)), "fused wgrad == wgrad kernel"
