@@ -18,8 +18,10 @@ algorithmic bytes / its average duration (HIP events on its stream);
 threads this process may use, at most 16 (one GPU's share of the host), with
 the host's CPU count and model recorded. ``kernels`` holds per-kernel
 durations inside the back-to-back steps; ``kernels_flushed`` the same
-kernels with 1 GiB written to scratch before each one (outside its event
-pair), so that none of its bytes come from L2 or the 256 MB Infinity Cache.
+kernels with 1 GiB of scratch written and read back before each one
+(outside its event pair), so that none of its bytes come from L2 or the
+256 MB Infinity Cache and no dirty lines of the flush are written back
+during it.
 ``outside_step`` times,
 outside the step, the backward of the combine fused with wgrad on the same
 buffers (dy in the expert layout + the routing-weight gradient), and the
@@ -91,7 +93,8 @@ def parse():
                          "one GPU's share of the host; 1: skip it)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-flushed per-op region")
     ap.add_argument("--flush-bytes", type=int, default=1 << 30,
-                    help="bytes written before every op of the cache-flushed region (>= 1 GiB evicts L2 and MALL)")
+                    help="bytes written and read back before every op of the cache-flushed region "
+                         "(>= 1 GiB evicts L2 and MALL)")
     ap.add_argument("--no-events", action="store_true", help="no per-kernel events inside the timed steps")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the fused combine backward")
     ap.add_argument("--no-router", action="store_true", help="skip timing the router gating")
@@ -578,19 +581,23 @@ def main():
 
     kernels = timed_steps() if use_ev else {}
     # Timed region 2b (cache-flushed per-kernel durations): the same K steps
-    # with --flush-bytes (1 GiB) written to a scratch buffer on the stream
-    # before every kernel, outside its event pair: L2 and the 256 MB Infinity
-    # Cache then hold none of the kernel's inputs, even those the kernel before
-    # it has just written.
+    # with --flush-bytes (1 GiB) of scratch written and then read back on the
+    # stream before every kernel, outside its event pair. The write evicts
+    # L2 and the 256 MB Infinity Cache (the kernel's inputs, even those the
+    # kernel before it has just written); the read then evicts the dirty
+    # lines the write leaves, so that their write-back does not fall inside
+    # the next kernel's events.
     kernels_flushed = None
     if use_ev and not args.no_flush:
         flush_buf = torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev)
+        flush_sum = torch.empty((), dtype=torch.float32, device=dev)
         fills = [0]
 
         def flush():
             fills[0] += 1
             with torch.cuda.stream(stream):
                 flush_buf.fill_(fills[0] & 255)
+                torch.sum(flush_buf.view(torch.float32), dim=0, out=flush_sum)
 
         kernels_flushed = timed_steps(flush)
         del flush_buf

@@ -386,8 +386,12 @@ static peg_status ensure_slots(int64_t T, int32_t K, int32_t E, int32_t layout, 
 #ifndef PEG_WGRAD_UMAX
 #define PEG_WGRAD_UMAX 2
 #endif
+// K <= 2 with rows of at most PEG_WGRAD_SPLIT vectors: 4 waves per token
+// (T4096 H4096 K2, inside the step: wgrad 15.5 us against 18.4 at 1, the
+// combine backward 33.1 against 34.4; with the caches flushed first both
+// within 1%).
 #ifndef PEG_WGRAD_WPT_K2
-#define PEG_WGRAD_WPT_K2 1
+#define PEG_WGRAD_WPT_K2 4
 #endif
 #ifndef PEG_WGRAD_UMAX_K2
 #define PEG_WGRAD_UMAX_K2 4
@@ -410,9 +414,9 @@ static RowShape combine_shape(int32_t K, int64_t nch) {
 #ifndef PEG_WGRAD_WPT_LONG
 #define PEG_WGRAD_WPT_LONG 4
 #endif
-// The same for K <= 2: 2 waves instead of 1 above PEG_WGRAD_SPLIT vectors
-// (T16384 H6144 K2: wgrad 66.5 us against 67.5, the combine backward 177.1
-// against 181.6; T4096 H4096 keeps 1: backward 35.2 us against 37.3).
+// The same for K <= 2 above PEG_WGRAD_SPLIT vectors: 2 waves (T16384 H6144
+// K2: wgrad 66.5 us against 67.5 at 1, the combine backward 177.1 against
+// 181.6).
 #ifndef PEG_WGRAD_WPT_K2_LONG
 #define PEG_WGRAD_WPT_K2_LONG 2
 #endif

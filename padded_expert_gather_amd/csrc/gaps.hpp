@@ -180,12 +180,12 @@ __device__ __forceinline__ void zero_gap_rows(uint8_t* __restrict__ out, int64_t
 // order: the access pattern of a plain fill, which HBM takes faster than
 // the long-lived gap blocks that share a launch with the token rows (T32768
 // H3584 E64 C4096: 1.29 GB of gap rows in 205 us, 6.3 TB/s).
-template <int VEC, int V, bool NT>
-__global__ __launch_bounds__(kBlock) void gap_fill_kernel(uint8_t* __restrict__ out, int64_t nch, int64_t out_rows,
-                                                          int32_t E, int32_t capacity,
-                                                          const int32_t* __restrict__ bins) {
-    using Vt = typename VecOf<VEC>::T;
-    const int e = blockIdx.y;
+// Block (x, e) of the fill: zeroes its chunk x of expert e's gap (e = E:
+// the rows past E*C).
+template <int VEC, bool NT>
+__device__ __forceinline__ void gap_fill_block(uint8_t* __restrict__ out, int64_t nch, int64_t out_rows, int32_t E,
+                                               int32_t capacity, const int32_t* __restrict__ bins, int e,
+                                               int64_t x, int v) {
     int64_t s, g;
     if (e >= E) {
         s = (int64_t)E * capacity;
@@ -199,20 +199,29 @@ __global__ __launch_bounds__(kBlock) void gap_fill_kernel(uint8_t* __restrict__ 
     if (g <= 0 || s < 0 || s >= out_rows) return;
     if (s + g > out_rows) g = out_rows - s;
     const int64_t units = g * nch;
-    const int64_t u0 = (int64_t)blockIdx.x * kBlock * V;
+    const int64_t u0 = x * kBlock * v;
     if (u0 >= units) return;
     uint8_t* dst = out + s * nch * VEC;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
+    for (int j = 0; j < 2; ++j) {
         const int64_t u = u0 + j * kBlock + threadIdx.x;
-        if (u < units) stream_store<VEC, NT>(dst, u, zero_vec<VEC>());
+        if (j < v && u < units) stream_store<VEC, NT>(dst, u, zero_vec<VEC>());
     }
+}
+
+template <int VEC, int V, bool NT>
+__global__ __launch_bounds__(kBlock) void gap_fill_kernel(uint8_t* __restrict__ out, int64_t nch, int64_t out_rows,
+                                                          int32_t E, int32_t capacity,
+                                                          const int32_t* __restrict__ bins) {
+    gap_fill_block<VEC, NT>(out, nch, out_rows, E, capacity, bins, blockIdx.y, blockIdx.x, V);
 }
 
 // Binned tensors of at least this many bytes get their gap rows from
 // gap_fill_kernel in a launch of its own before the token rows (measured:
 // T32768 H3584 E64 C4096 gather 397 -> 359 us, T16384 H6144 E8 C5120 127 ->
-// 122 us; the T512 H250 f32 tensor of 1 MB is faster in one launch).
+// 122 us; the T512 H250 f32 tensor of 1 MB is faster in one launch). The
+// same fill blocks placed at the front of the token kernel's own grid took
+// 413 us at T32768 H3584 against 320 for the two launches.
 #ifndef PEG_GAP_FILL_MIN_BYTES
 #define PEG_GAP_FILL_MIN_BYTES (int64_t(128) << 20)
 #endif
@@ -221,21 +230,35 @@ inline bool use_gap_fill(int32_t layout, int64_t out_rows, int64_t row_bytes, in
     return layout == PEG_BINNED && out_rows * row_bytes >= PEG_GAP_FILL_MIN_BYTES && E < 65535;
 }
 
-// Launches gap_fill_kernel over the binned tensor `out` of out_rows rows
-// (nch vectors of VEC bytes each); rows past E*C are zeroed too.
-// Vectors per thread: 1 for rows of at most 512 vectors, else 2 (T32768
+// Shape of the fill over a binned tensor of out_rows rows of nch vectors:
+// gx chunks per expert, ey experts (E, or E + 1 with rows past E*C), v
+// vectors per thread: 1 for rows of at most 512 vectors, else 2 (T32768
 // H3584: 205 us at 1 against 219 at 2; T16384 H6144: 42 us at 2 against 52
-// at 1). Stores carry the nontemporal hint (3-5% faster here).
+// at 1).
+struct GapFillShape {
+    int64_t gx;
+    int ey, v;
+};
+inline GapFillShape gap_fill_shape(int64_t nch, int64_t out_rows, int32_t E, int32_t capacity) {
+    const int64_t tail = out_rows - (int64_t)E * capacity;
+    const int64_t max_rows = tail > capacity ? tail : capacity;
+    const int v = nch <= 512 ? 1 : 2;
+    const int64_t gx = (max_rows * nch + (int64_t)kBlock * v - 1) / ((int64_t)kBlock * v);
+    return GapFillShape{gx > 0 ? gx : 0, E + (tail > 0 ? 1 : 0), v};
+}
+
+// Launches gap_fill_kernel over the binned tensor `out` of out_rows rows
+// (nch vectors of VEC bytes each); rows past E*C are zeroed too. Stores
+// carry the nontemporal hint (3-5% faster here).
 template <int VEC>
 inline peg_status launch_gap_fill(uint8_t* out, int64_t nch, int64_t out_rows, int32_t E, int32_t capacity,
                                   const int32_t* bins, hipStream_t s) {
-    const int64_t tail = out_rows - (int64_t)E * capacity;
-    const int64_t max_rows = tail > capacity ? tail : capacity;
-    const int V = nch <= 512 ? 1 : 2;
-    const int64_t gx = (max_rows * nch + (int64_t)kBlock * V - 1) / ((int64_t)kBlock * V);
+    const GapFillShape f = gap_fill_shape(nch, out_rows, E, capacity);
+    const int V = f.v;
+    const int64_t gx = f.gx;
     if (gx <= 0) return PEG_OK;
     if (!grid_fits(gx, kBlock)) return PEG_ERR_BAD_SHAPE;
-    const dim3 grid((unsigned)gx, (unsigned)(E + (tail > 0 ? 1 : 0)));
+    const dim3 grid((unsigned)gx, (unsigned)f.ey);
     if (V == 1) return launch(gap_fill_kernel<VEC, 1, true>, grid, dim3(kBlock), 0, s, out, nch, out_rows, E, capacity, bins);
     return launch(gap_fill_kernel<VEC, 2, true>, grid, dim3(kBlock), 0, s, out, nch, out_rows, E, capacity, bins);
 }
