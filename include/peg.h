@@ -143,10 +143,10 @@ peg_status peg_route_prep(const int32_t* top_experts, int64_t T, int32_t K, int3
  * more) is a static array of PEG_NOALLOC_SCRATCH_BYTES in the library's
  * device memory, one per GPU.
  *   Limit: the count table takes ceil(T*K / tile) * E * 4 bytes, the tile
- *   being 2048 assignments for E <= 256, 1024 for E <= 512, 512 above (and
- *   smaller for batches under 64 tiles); sizes beyond the scratch return
- *   PEG_ERR_SCRATCH_LIMIT and enqueue nothing. The scratch holds up to
- *   2,097,152 assignments at E = 256 and 131,072 at E = 1024.
+ *   being 1024 assignments for E <= 512 and 512 above (smaller for batches
+ *   under 64 tiles); sizes beyond the scratch return PEG_ERR_SCRATCH_LIMIT
+ *   and enqueue nothing. The scratch holds up to 4,194,304 assignments at
+ *   E = 64, 1,048,576 at E = 256 and 131,072 at E = 1024.
  *   The scratch needs no clearing (every entry a call reads, it writes
  *   first). Every call on one GPU uses that GPU's one array: calls that may
  *   overlap on one GPU (other streams, other host threads) race and must be

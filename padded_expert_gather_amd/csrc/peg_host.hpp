@@ -114,11 +114,11 @@ inline int64_t token_blocks(int64_t T, int wpt) {
 #ifndef PEG_MIN_TILES
 #define PEG_MIN_TILES 64
 #endif
-// Ids per thread of a tile are capped at PEG_PREP_ITEMS_MAX. Measured
-// (route_prep alone): T32768 K8 E64 17.5 us at 8 against 21.0 at 16 and 20.1
-// at 4; the other workloads move by less than 0.1 us.
+// Ids per thread of a tile are capped at PEG_PREP_ITEMS_MAX. Measured (in
+// the step): T32768 K8 E64 14.3 us at 4 against 15.1 at 8; T8192 K8 E256 and
+// T4096 K2 E8 move by less than 0.1 us.
 #ifndef PEG_PREP_ITEMS_MAX
-#define PEG_PREP_ITEMS_MAX 8
+#define PEG_PREP_ITEMS_MAX 4
 #endif
 inline int prep_items(int32_t E) {
     const int items = E <= 128 ? 16 : (E <= 256 ? 8 : (E <= 512 ? 4 : 2));

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
 // at most kMergedMaxTable ints); block 0 also writes tokens_per_expert,
 // bins and padded_bins.
 // SB: table loads each placement thread keeps in flight while summing the
-// table (1, 4 or 32: about the tiles one thread sums).
+// table (1, 4 or 32: about the tiles one thread sums; 64 at once measured
+// 16.2 against 14.4 us at T8192 K8 E256).
 template <int ITEMS, int SB>
 __global__ __launch_bounds__(kBlock) void tile_place_kernel(
     const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, const int32_t* __restrict__ counts,

@@ -43,8 +43,8 @@ def test_version_status_and_workspace(lib):
     assert lib.peg_workspace_bytes(-1, 2, 8) == 0
     assert lib.peg_workspace_bytes(10, 0, 8) == 0
     assert lib.peg_workspace_bytes(10, 2, 2000) == 0
-    # route_prep tiles of 2048 ids at E <= 256: 65536 ids -> 32 tiles * 256 experts * 4 B
-    assert lib.peg_workspace_bytes(8192, 8, 256) >= 32 * 256 * 4
+    # route_prep tiles of 1024 ids at E <= 512: 65536 ids -> 64 tiles * 256 experts * 4 B
+    assert lib.peg_workspace_bytes(8192, 8, 256) >= 64 * 256 * 4
     # slot-row rebuild needs T*K int32
     assert lib.peg_workspace_bytes(4096, 2, 8) >= 4096 * 2 * 4
     assert lib.peg_workspace_bytes(0, 1, 1) == 256
@@ -104,7 +104,7 @@ def test_route_prep_noalloc_checks(lib):
     # E = 1024 tiles hold 512 assignments: 131,073 of them need 257 tiles of
     # 1024 counts (1,052,672 bytes), past the 1 MiB scratch
     assert call(T=131073, K=1, E=1024, C=200) == SCRATCH_LIMIT
-    assert call(T=(1 << 20) + 256, K=8, E=64, C=200) == SCRATCH_LIMIT  # 4097 tiles of 2048 x 64
+    assert call(T=(1 << 19) + 128, K=8, E=64, C=200) == SCRATCH_LIMIT  # 4097 tiles of 1024 x 64 counts
 
 
 def test_gather_checks(lib):
