@@ -79,6 +79,10 @@ CASES = [
     _case("tiled_32768", 16384, 2, 8, 8, W.BF16, B, cap=5000, skew=0.3),
     _case("tiled_32770", 16385, 2, 8, 8, W.BF16, P, m=64),
     _case("small_unstaged", 4000, 2, 64, 8, W.BF16, B, cap=100),
+    _case("tiled_E16_ragged", 5001, 3, 16, 24, W.BF16, P, m=8, none_frac=0.1, skew=0.2),
+    _case("tiled_E1", 10000, 1, 1, 16, W.BF16, B, cap=5000),
+    _case("tiled_16384_E13", 8192, 2, 13, 8, W.BF16, B, cap=900, skew=0.5),
+    _case("tiled_16386_E16", 8193, 2, 16, 8, W.BF16, P, m=4),
     _case("tile_2048", 1024, 2, 8, 16, W.BF16, B, cap=300),
     _case("tile_2049", 683, 3, 8, 16, W.BF16, P, m=8),
     _case("tile_2047", 2047, 1, 8, 16, W.BF16, B, cap=300),

@@ -5,7 +5,8 @@ backward.
 
 Every output buffer is filled with 0xFF bytes first, so a gap row that is
 not written shows up as a mismatch. Cases: 16-, 8-, 4- and 2-byte row
-vectors; binned with dropped routes and mostly empty capacity; padded with a
+vectors, binned tensors above and below 128 MB (the gap rows of the former
+come from a fill-shaped launch of their own); binned with dropped routes and mostly empty capacity; padded with a
 large multiple; padded with a multiple of 2 and a buffer far longer than the
 padded rows, so that each gap block's range crosses the gaps of many
 experts (rows past padded_bins[E-1] must stay untouched); a buffer cut short
@@ -49,6 +50,7 @@ def _filled(rows, H, dtype):
     (60000, 2, 64, 12, W.BF16, 98304, 0.1, 0.0),     # 8-byte vectors
     (80000, 2, 32, 7, W.F32, 262144, 0.0, 0.5),      # 4-byte vectors
     (50000, 8, 64, 5, W.BF16, 65536, 0.0, 2.0),      # 2-byte vectors, heavy skew
+    (50000, 8, 64, 5, W.BF16, 262144, 0.0, 2.0),     # 2-byte vectors, 168 MB: the fill-shaped gap launch
     (300000, 1, 1, 256, W.BF16, 524288, 0.2, 0.0),   # E = 1
     (20000, 2, 64, 64, W.BF16, 32768, 1.0, 0.0),     # no route at all: every row is gap
 ])
