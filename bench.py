@@ -22,8 +22,9 @@ kernels with 1 GiB of scratch written and read back before each one
 (outside its event pair), so that none of its bytes come from L2 or the
 256 MB Infinity Cache and no dirty lines of the flush are written back
 during it.
-``outside_step`` times,
-outside the step, the backward of the combine fused with wgrad on the same
+``outside_step`` times (back to back, and with the caches flushed before
+each launch),
+outside the step, the backward of the combine with wgrad on the same
 buffers (dy in the expert layout + the routing-weight gradient), and the
 router top-k gating (softmax, renormalised) of the workload's router scores,
 alone and fused with route_prep.
@@ -588,6 +589,7 @@ def main():
     # lines the write leaves, so that their write-back does not fall inside
     # the next kernel's events.
     kernels_flushed = None
+    flush = None
     if use_ev and not args.no_flush:
         flush_buf = torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev)
         flush_sum = torch.empty((), dtype=torch.float32, device=dev)
@@ -600,7 +602,6 @@ def main():
                 torch.sum(flush_buf.view(torch.float32), dim=0, out=flush_sum)
 
         kernels_flushed = timed_steps(flush)
-        del flush_buf
     dominant = max(ab, key=lambda n: kernels[n]["avg_us"]) if use_ev else None
     roofline = None
     if dominant:
@@ -619,21 +620,34 @@ def main():
         for i in range(max(2, args.warmup)):
             steps_obj[i % sets].run_extra(name)
         torch.cuda.synchronize()
-        bevs = [(hip.create(), hip.create()) for _ in range(args.steps)]
-        for i in range(args.steps):
-            steps_obj[i % sets].run_extra(name, bevs[i], hip)
-        torch.cuda.synchronize()
-        ms = [hip.elapsed_ms(a, b) for a, b in bevs]
-        avg = sum(ms) / len(ms)
+
+        def timed_extra(before=None):
+            bevs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+            for i in range(args.steps):
+                if before is not None:
+                    before()
+                steps_obj[i % sets].run_extra(name, bevs[i], hip)
+            torch.cuda.synchronize()
+            ms = [hip.elapsed_ms(a, b) for a, b in bevs]
+            return ms, sum(ms) / len(ms)
+
+        ms, avg = timed_extra()
         bb = extra_bytes[name]
         extras[name] = {"avg_us": round(avg * 1e3, 2), "median_us": round(median(ms) * 1e3, 2),
                         "min_us": round(min(ms) * 1e3, 2), "bytes": bb,
                         "GBps": round(bb / (avg / 1e3) / 1e9, 1),
                         "frac_peak": round(bb / (avg / 1e3) / 1e9 / PEAK_GBS, 4)}
+        if flush is not None:
+            # the same launches with the caches flushed before each one
+            _, avg_f = timed_extra(flush)
+            extras[name]["avg_us_flushed"] = round(avg_f * 1e3, 2)
+            extras[name]["frac_peak_flushed"] = round(bb / (avg_f / 1e3) / 1e9 / PEAK_GBS, 4)
         if name == "combine_backward":
             extras[name]["traffic"] = traffic_for("backward", wl.name)
         if name in ("router_topk", "route_prep_logits"):
             extras[name]["tokens_per_s"] = round(wl.T / (avg / 1e3), 1)
+    if flush is not None:
+        del flush_buf
     ceilings = copy_ceiling(torch, HipEvents(), stream) if not args.no_events else None
     if roofline and ceilings:
         roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / ceilings["copy"], 4)

@@ -436,9 +436,10 @@ def wgrad(y, grad, r, out=None, ws=None, use_slot_row=True):
 
 
 def combine_backward(y, dout, r, weights=None, dy=None, dy_rows=None, wgrad_out=None, ws=None, use_slot_row=True):
-    """Backward of the combine fused with wgrad: returns (dy, wgrad) where
+    """Backward of the combine with wgrad: returns (dy, wgrad) where
     dy[row(a)] = w[a] * dout[t] in the expert layout (gap rows zero; a raw copy
-    when weights is None) and wgrad [T, K] f32 = <y[row(a)], dout[t]>."""
+    when weights is None) and wgrad [T, K] f32 = <y[row(a)], dout[t]>.
+    One fused pass for K <= 2; for larger K a dy gather, then the wgrad kernel."""
     y = _dev(y, "y")
     _expert_tensor(y, r, "y")
     dout = _dev(dout, "dout", y.dtype)

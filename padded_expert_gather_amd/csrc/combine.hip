@@ -327,6 +327,91 @@ __global__ __launch_bounds__(kBlock) PEG_WGRAD_OCCUPANCY void combine_backward_k
 #undef PEG_WGRAD_PARAMS
 #undef PEG_WGRAD_ARGS
 
+// dy of the combine backward as a weighted gather of dout (used for K > 2,
+// with wgrad then computed by wgrad_kernel): the WPT waves of a token read
+// its dout row once, in slices, and store it into each of its kept rows of
+// dy - scaled by the route's weight and rounded once (DY == 2) or as raw
+// bits (DY == 1). Blocks past token_blocks zero dy's gap rows and the rows
+// past the layout's R.
+template <int DT, int VEC, int U, int WPT, int DY>
+__global__ __launch_bounds__(kBlock) void dy_gather_kernel(
+    const uint8_t* __restrict__ dout, uint8_t* __restrict__ dy, int64_t nch, int64_t slice, int64_t T, int32_t K,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ weights, int64_t dy_rows, int32_t layout,
+    int32_t E, int32_t capacity, const int32_t* __restrict__ bins, const int32_t* __restrict__ padded_bins,
+    int64_t token_blocks) {
+    using L = Lanes<DT, VEC>;
+    using V = typename L::V;
+    constexpr int N = L::N;
+    const int64_t nz = (int64_t)gridDim.x - token_blocks;
+    int64_t role_index;
+    if (gap_role(blockIdx.x, gridDim.x, nz, &role_index)) {
+        zero_gap_rows<VEC, PEG_NT_STORE_DY_ZERO>(dy, nch, dy_rows, layout, E, capacity, bins, padded_bins,
+                                                  role_index, nz, true);
+        return;
+    }
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t gw = role_index * (kBlock / kWave) + w;  // wave of the launch
+    const int64_t t = gw / WPT;
+    if (t >= T) return;  // no barrier in the token part
+    const int lane = lane_id();
+    const int64_t c_begin = (gw % WPT) * slice;
+    const int64_t c_end = c_begin + slice < nch ? c_begin + slice : nch;
+    const int32_t* my_rows = slot_row + t * K;
+    int r8[kRowsFast];
+    float w8[kRowsFast];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < kRowsFast; ++k) {
+        const int r = k < K ? my_rows[k] : -1;
+        r8[k] = (r >= 0 && r < dy_rows) ? r : -1;
+        w8[k] = (DY == 2 && r8[k] >= 0) ? weights[t * K + k] : 1.0f;
+        any |= r8[k] >= 0;
+    }
+    for (int k = kRowsFast; k < K; ++k) {
+        const int r = my_rows[k];
+        any |= r >= 0 && r < dy_rows;
+    }
+    if (!any) return;  // no kept route: nothing to store
+    const int64_t row_bytes = nch * VEC;
+    const uint8_t* src = dout + t * row_bytes;
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += (int64_t)kWave * U) {
+        V v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u * kWave + lane;
+            if (c < c_end) v[u] = stream_load<VEC>(src, c);
+        }
+        for (int k = 0; k < K; ++k) {
+            int r;
+            float wk;
+            if (k < kRowsFast) {
+                r = r8[k];
+                wk = w8[k];
+            } else {
+                r = my_rows[k];
+                r = (r >= 0 && r < dy_rows) ? r : -1;
+                wk = (DY == 2 && r >= 0) ? weights[t * K + k] : 1.0f;
+            }
+            if (r < 0) continue;
+            uint8_t* drow = dy + (int64_t)r * row_bytes;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u * kWave + lane;
+                if (c >= c_end) continue;
+                if constexpr (DY == 1) {
+                    stream_store<VEC>(drow, c, v[u]);
+                } else {
+                    float f[N];
+                    L::unpack(v[u], f);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) f[i] = wk * f[i];
+                    stream_store<VEC>(drow, c, L::pack(f));
+                }
+            }
+        }
+    }
+}
+
 struct RowArgs {
     int64_t static_rows;
     const int32_t* padded_bins;
@@ -579,6 +664,103 @@ static peg_status wgrad_by_dtype(int32_t dtype, int vec, int u, dim3 grid, hipSt
     return wgrad_dispatch<PEG_F16, DY>(vec, u, grid, s, a);
 }
 
+// wgrad_kernel over a valid row map (the launch of peg_wgrad after its
+// checks); vec: the row-vector width of y and grad.
+static peg_status wgrad_launch(const void* y, const void* grad, int32_t dtype, int vec, int32_t layout, int64_t T,
+                               int64_t H, int32_t K, int32_t E, int32_t capacity, const int32_t* bins,
+                               const int32_t* padded_bins, const int32_t* slot_row, float* wgrad, hipStream_t s) {
+    const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
+                     layout == PEG_PADDED ? padded_bins : nullptr};
+    const int64_t nch = H * elem_bytes(dtype) / vec;
+    const RowShape sh = wgrad_shape(K, nch);
+    const int64_t q = wave_slice(nch, sh.wpt);
+    const int u = pass_vectors(q, sh.umax);
+    const int64_t tb = token_blocks(T, sh.wpt);
+    const WgradArgs a{(const uint8_t*)y, (const uint8_t*)grad, wgrad, nch, q, T, K, slot_row, ra, E, nullptr,
+                      nullptr, 0, layout, capacity, bins, tb, sh.wpt};
+    if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
+    return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
+}
+
+// Waves per token of dy_gather_kernel: as the gather's (2 up to 512 row
+// vectors, else 4).
+struct DyArgs {
+    const uint8_t* dout;
+    uint8_t* dy;
+    int64_t nch, slice, T;
+    int32_t K;
+    const int32_t* slot_row;
+    const float* weights;
+    int64_t dy_rows;
+    int32_t layout, E, capacity;
+    const int32_t* bins;
+    const int32_t* padded_bins;
+    int64_t token_blocks;
+};
+
+template <int DT, int VEC, int DY>
+static peg_status dy_gather_go(int wpt, int u, dim3 grid, hipStream_t s, const DyArgs& a) {
+#define PEG_DY_LAUNCH(WPT, UU)                                                                                  \
+    return launch(dy_gather_kernel<DT, VEC, UU, WPT, DY>, grid, dim3(kBlock), 0, s, a.dout, a.dy, a.nch, a.slice, \
+                  a.T, a.K, a.slot_row, a.weights, a.dy_rows, a.layout, a.E, a.capacity, a.bins, a.padded_bins,   \
+                  a.token_blocks)
+    if (wpt == 2) {
+        if (u == 1) PEG_DY_LAUNCH(2, 1);
+        if (u == 2) PEG_DY_LAUNCH(2, 2);
+        PEG_DY_LAUNCH(2, 4);
+    }
+    if (u == 1) PEG_DY_LAUNCH(4, 1);
+    if (u == 2) PEG_DY_LAUNCH(4, 2);
+    PEG_DY_LAUNCH(4, 4);
+#undef PEG_DY_LAUNCH
+}
+
+template <int DT, int DY>
+static peg_status dy_gather_vec(int vec, int wpt, int u, dim3 grid, hipStream_t s, const DyArgs& a) {
+    switch (vec) {
+        case 16: return dy_gather_go<DT, 16, DY>(wpt, u, grid, s, a);
+        case 8: return dy_gather_go<DT, 8, DY>(wpt, u, grid, s, a);
+        case 4: return dy_gather_go<DT, 4, DY>(wpt, u, grid, s, a);
+        default:
+            if constexpr (Elem<DT>::bytes == 2) return dy_gather_go<DT, 2, DY>(wpt, u, grid, s, a);
+            return PEG_ERR_ALIGNMENT;
+    }
+}
+
+// dy of the combine backward by dy_gather_kernel, its gap rows zeroed as the
+// gather zeroes its own (a fill-shaped launch first for a binned dy of 128 MB
+// and more, else trailing gap blocks).
+static peg_status dy_gather(const void* dout, const float* weights, int32_t dtype, int vec, int32_t layout,
+                            int64_t T, int64_t H, int32_t K, int32_t E, int32_t capacity, const int32_t* bins,
+                            const int32_t* padded_bins, const int32_t* slot_row, void* dy, int64_t dy_rows,
+                            hipStream_t s) {
+    const int64_t row_bytes = H * elem_bytes(dtype);
+    const int64_t nch = row_bytes / vec;
+    const bool fill = dy_rows > 0 && use_gap_fill(layout, dy_rows, row_bytes, E);
+    const int64_t nz = fill ? 0 : gap_blocks(dy_rows, nch);
+    const int wpt = nch <= 512 ? 2 : 4;
+    const int64_t tb = token_blocks(T, wpt);
+    if (!grid_fits(tb + nz, kBlock)) return PEG_ERR_BAD_SHAPE;
+    if (fill) PEG_CHECK(launch_gap_fill_vec(vec, (uint8_t*)dy, nch, dy_rows, E, capacity, bins, s));
+    const int64_t slice = wave_slice(nch, wpt);
+    const int u = lanes_per_pass(slice);
+    const DyArgs a{(const uint8_t*)dout, (uint8_t*)dy, nch, slice, T, K, slot_row, weights, dy_rows, layout, E,
+                   capacity, bins, padded_bins, tb};
+    const dim3 grid((unsigned)(tb + nz));
+    if (weights) {
+        if (dtype == PEG_F32) return dy_gather_vec<PEG_F32, 2>(vec, wpt, u, grid, s, a);
+        if (dtype == PEG_BF16) return dy_gather_vec<PEG_BF16, 2>(vec, wpt, u, grid, s, a);
+        return dy_gather_vec<PEG_F16, 2>(vec, wpt, u, grid, s, a);
+    }
+    return dy_gather_vec<PEG_BF16, 1>(vec, wpt, u, grid, s, a);  // raw bits: the type plays no part
+}
+
+// K above this: the combine backward runs as dy_gather_kernel then
+// wgrad_kernel instead of one fused pass.
+#ifndef PEG_BACKWARD_SPLIT_K
+#define PEG_BACKWARD_SPLIT_K 2
+#endif
+
 }  // namespace peg
 
 using namespace peg;
@@ -618,17 +800,7 @@ PEG_API peg_status peg_wgrad(const void* y, const void* grad, int32_t dtype, int
     if (vec == 0) return PEG_ERR_ALIGNMENT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     PEG_CHECK(ensure_slots(T, K, E, layout, capacity, indices, bin_ids, bins, padded_bins, &slot_row, ws, ws_bytes, s));
-    const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
-                     layout == PEG_PADDED ? padded_bins : nullptr};
-    const int64_t nch = H * eb / vec;
-    const RowShape sh = wgrad_shape(K, nch);
-    const int64_t q = wave_slice(nch, sh.wpt);
-    const int u = pass_vectors(q, sh.umax);
-    const int64_t tb = token_blocks(T, sh.wpt);
-    const WgradArgs a{(const uint8_t*)y, (const uint8_t*)grad, wgrad, nch, q, T, K, slot_row, ra, E, nullptr,
-                      nullptr, 0, layout, capacity, bins, tb, sh.wpt};
-    if (!grid_fits(tb, kBlock)) return PEG_ERR_BAD_SHAPE;
-    return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
+    return wgrad_launch(y, grad, dtype, vec, layout, T, H, K, E, capacity, bins, padded_bins, slot_row, wgrad, s);
 }
 
 PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const float* weights, int32_t dtype,
@@ -648,6 +820,12 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     if (vec == 0) return PEG_ERR_ALIGNMENT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     PEG_CHECK(ensure_slots(T, K, E, layout, capacity, indices, bin_ids, bins, padded_bins, &slot_row, ws, ws_bytes, s));
+    if (K > PEG_BACKWARD_SPLIT_K) {
+        PEG_CHECK(dy_gather(dout, weights, dtype, vec, layout, T, H, K, E, capacity, bins, padded_bins, slot_row, dy,
+                            dy_rows, s));
+        return wgrad_launch(y, dout, dtype, vec, layout, T, H, K, E, capacity, bins, padded_bins, slot_row, wgrad,
+                            s);
+    }
     const RowArgs ra{layout == PEG_BINNED ? (int64_t)E * capacity : 0,
                      layout == PEG_PADDED ? padded_bins : nullptr};
     const int64_t nch = H * eb / vec;

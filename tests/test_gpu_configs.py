@@ -84,7 +84,7 @@ def test_small_configs_full(cid, seed):
     assert_close(to_host(peg.scatter_combine(yrg, rg, weights=w_g)), so2, S2, wl.dtype, "combine(y_rand)")
     wo2, WS2 = oracle.wgrad(yr, wl.grad, wl.dtype, ro, wl.layout, cap, with_scale=True)
     assert_close(to_host(peg.wgrad(yrg, gg, rg)), wo2, WS2, W.F32, "wgrad(y_rand)")
-    # backward of the combine fused with wgrad, upstream gradient = wl.grad
+    # backward of the combine with wgrad, upstream gradient = wl.grad
     dyo = oracle.combine_backward_dy(wl.grad, wl.dtype, ro, wl.layout, cap, weights=w_o)
     dyg, wgb = peg.combine_backward(yrg, gg, rg, weights=w_g, dy_rows=R)
     assert_close(to_host(dyg), dyo, np.abs(W.to_f32(dyo, wl.dtype).astype(np.float64)), wl.dtype, "backward dy")
@@ -187,7 +187,7 @@ def test_large_config(cid, seed):
         assert_close(to_host(wr[tg]), wo2, WS2, W.F32, f"wgrad(y_rand) {what}")
         del yr, yrg
         print(f"[config {cid}] independent y ok", flush=True)
-    # backward of the combine fused with wgrad: every kept row of dy equals
+    # backward of the combine with wgrad: every kept row of dy equals
     # the fp32 product w * dout rounded once (computed here by torch on the
     # device), every other row is zero; the fused wgrad equals the wgrad
     # kernel bit for bit; a row sample against the oracle

@@ -165,7 +165,7 @@ def test_edge_case(c):
     assert_close(to_host(peg.wgrad(yrg, gg, rg, use_slot_row=False)), wo, WS, W.F32, "wgrad rebuilt map")
     wo2, WS2 = oracle.wgrad(yo, grad, dtype, ro, layout, cap, with_scale=True)
     assert_close(to_host(peg.wgrad(yg, gg, rg)), wo2, WS2, W.F32, "wgrad(gather(x))")
-    # --- backward of the combine fused with wgrad (dout = grad)
+    # --- backward of the combine with wgrad (dout = grad)
     check_combine_backward(yrg, yr, grad, gg, w, wg, ro, rg, layout, cap, dtype, R)
     # --- the validator accepts what route_prep built
     assert int(peg.validate_routing(rg, n_indices=ro.n).item()) == 0
@@ -335,13 +335,16 @@ def test_binding_refuses_bad_buffers():
     assert int(peg.validate_routing(rg).item()) == 0                   # the routing itself is intact
 
 
+@pytest.mark.parametrize("K", [2, 4])
 @pytest.mark.parametrize("layout", [W.BINNED, W.PADDED])
-def test_combine_backward_rows_past_layout(layout):
+def test_combine_backward_rows_past_layout(layout, K):
     """dy with more rows than the layout's R: the kept rows and gaps as
     usual, and every row of [R, dy_rows) zero (the buffer starts as a
-    sentinel); nothing is written past dy_rows."""
-    rng = np.random.default_rng(11 + layout)
-    T, K, E, H, C, m = 150, 2, 6, 72, 40, 8
+    sentinel); nothing is written past dy_rows. K = 2 runs the fused pass,
+    K = 4 the dy gather followed by the wgrad kernel."""
+    print(f"[backward past layout] layout{layout} K{K}", flush=True)
+    rng = np.random.default_rng(11 + layout + 7 * K)
+    T, E, H, C, m = 150, 6, 72, 20 * K, 8
     top, w = W.random_routing(rng, T, K, E, skew=0.3, none_frac=0.1)
     grad = W.normal(rng, (T, H), W.BF16)
     cap = C if layout == W.BINNED else None
@@ -358,6 +361,38 @@ def test_combine_backward_rows_past_layout(layout):
     bits_equal(to_host(dyg[:R]), dyo, "dy rows [0, R)")
     assert int(buf[R: R + extra].view(torch.int16).count_nonzero().item()) == 0, "rows [R, dy_rows) not zero"
     assert bool((buf[R + extra:] == -7.0).all()), "a row past dy_rows was written"
+
+
+@pytest.mark.parametrize("K", [2, 4])
+@pytest.mark.parametrize("layout", [W.BINNED, W.PADDED])
+def test_combine_backward_short_dy(layout, K):
+    """dy with fewer rows than the layout's R: rows [0, dy_rows) as the
+    oracle's (kept rows w * dout, gaps zero), nothing written at or past
+    dy_rows, and wgrad still computed for the routes whose rows lie there
+    (equal, bit for bit, to the wgrad kernel's)."""
+    print(f"[backward short dy] layout{layout} K{K}", flush=True)
+    rng = np.random.default_rng(40 + layout + 7 * K)
+    T, E, H, C, m = 200, 5, 136, 30 * K, 8
+    top, w = W.random_routing(rng, T, K, E, skew=0.3, none_frac=0.1)
+    grad = W.normal(rng, (T, H), W.BF16)
+    cap = C if layout == W.BINNED else None
+    ro = oracle.route_prep(top, E, pad_multiple=m)
+    rg = peg.route_prep(to_dev(top), E, capacity=cap, pad_multiple=None if cap else m)
+    R = oracle.expert_rows(ro, layout, cap)
+    rows = oracle.assignment_rows(ro, layout, cap)
+    short = R // 2 + 3
+    assert 0 < short < R and (rows >= short).any()
+    yr = W.expert_tensor_rows(rng, R, H, W.BF16, used_rows=rows[rows >= 0])
+    yrg, gg, wg = to_dev(yr, W.BF16), to_dev(grad, W.BF16), to_dev(w.reshape(-1))
+    buf = torch.full((R, H), -7.0, dtype=torch.bfloat16, device=DEV)
+    dyg, wgb = peg.combine_backward(yrg, gg, rg, weights=wg, dy=buf[:short], use_slot_row=True)
+    dyo = oracle.combine_backward_dy(grad, W.BF16, ro, layout, cap, weights=w.reshape(-1))
+    assert_close(to_host(dyg), dyo[:short], np.abs(W.to_f32(dyo[:short], W.BF16).astype(np.float64)), W.BF16,
+                 "dy rows [0, dy_rows)")
+    assert bool((buf[short:] == -7.0).all()), "a row at or past dy_rows was written"
+    wo, WS = oracle.wgrad(yr, grad, W.BF16, ro, layout, cap, with_scale=True)
+    assert_close(to_host(wgb), wo, WS, W.F32, "wgrad with a short dy")
+    bits_equal(to_host(wgb), to_host(peg.wgrad(yrg, gg, rg)), "wgrad with a short dy == wgrad kernel")
 
 
 def test_gather_padded_refuses_binned_routing():

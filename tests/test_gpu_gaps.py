@@ -178,14 +178,16 @@ def test_tensor_beyond_2gib():
     assert torch.equal(wgb, wgr), "fused wgrad == wgrad kernel"
 
 
-def test_large_binned_dy_rows_past_layout():
+@pytest.mark.parametrize("K", [2, 4])
+def test_large_binned_dy_rows_past_layout(K):
     """The combine backward into a binned dy of more than 128 MB (its gap
     rows then come from the fill-shaped launch) with more rows than E*C:
     kept rows are w * dout, gap rows and the rows [E*C, dy_rows) are zero,
-    rows past dy_rows untouched; the fused wgrad equals the wgrad kernel."""
-    print("[gaps dy tail]", flush=True)
-    rng = np.random.default_rng(31)
-    T, K, E, H, C = 20000, 2, 8, 2048, 4096
+    rows past dy_rows untouched; the fused wgrad (K = 2) or the wgrad
+    kernel's pass after the dy gather (K = 4) equals the wgrad kernel."""
+    print(f"[gaps dy tail] K{K}", flush=True)
+    rng = np.random.default_rng(31 + K)
+    T, E, H, C = 20000, 8, 2048, 4096
     extra = 1000
     assert E * C * H * 2 >= 128 << 20
     top, w = W.random_routing(rng, T, K, E, none_frac=0.05, skew=0.4)
