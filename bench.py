@@ -124,8 +124,10 @@ def copy_calibration(torch):
 def copy_ceiling(torch, hip, tstream):
     """Streaming rates of this GPU measured with torch's own kernels on 1 GiB
     buffers, timed with HIP events (median of 5): device-to-device copy (read
-    + write bytes per second), fill (write only) and a float32 sum (read
-    only). Returns {"copy": GB/s, "write": GB/s, "read": GB/s}."""
+    + write bytes per second), fill (write only), a float32 sum (read only)
+    and a bfloat16 add of two buffers into a third (two bytes read per byte
+    written). Returns {"copy": GB/s, "write": GB/s, "read": GB/s,
+    "add": GB/s}."""
     n = 1 << 30
     stream = ctypes.c_void_p(tstream.cuda_stream)
     with torch.cuda.stream(tstream):
@@ -150,9 +152,12 @@ def copy_ceiling(torch, hip, tstream):
         t_copy = timed(lambda: dst.copy_(src))
         t_fill = timed(lambda: dst.fill_(3))
         t_sum = timed(lambda: src.view(torch.float32).sum())
-    del src, dst
+        src2 = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(2)
+        a16, b16, c16 = src.view(torch.bfloat16), src2.view(torch.bfloat16), dst.view(torch.bfloat16)
+        t_add = timed(lambda: torch.add(a16, b16, out=c16))
+    del src, src2, dst
     return {"copy": round(2 * n / t_copy / 1e9, 1), "write": round(n / t_fill / 1e9, 1),
-            "read": round(n / t_sum / 1e9, 1)}
+            "read": round(n / t_sum / 1e9, 1), "add": round(3 * n / t_add / 1e9, 1)}
 
 
 def median(xs):
