@@ -4,8 +4,9 @@ batch (the small workload, so the run takes seconds).
 The line must be one JSON object with the metric, a positive throughput on one
 GPU, the workload named in ``config``, and a ``roofline`` object whose
 fraction is its achieved rate over MI355X's 8 TB/s, per-kernel durations in
-the back-to-back steps and with the caches flushed; the CPU legs are skipped
-here (tests/test_host.py covers them on the CPU).
+the back-to-back steps and with the caches flushed, torch's streaming rates,
+and the combine backward outside the step; the CPU legs are skipped here
+(tests/test_host.py covers them on the CPU).
 """
 import json
 import os
@@ -41,3 +42,9 @@ def test_bench_line():
         assert rec["kernels"][op]["avg_us"] > 0, op
         assert rec["kernels_flushed"][op]["avg_us"] > 0, op
     assert rec["flush_bytes"] >= 1 << 30
+    # torch's own streaming kernels as reference rates, and the out-of-step
+    # calls timed back to back and cache-flushed
+    assert set(rec["streaming_GBps"]) == {"copy", "write", "read", "add"}
+    assert all(v > 0 for v in rec["streaming_GBps"].values())
+    cb = rec["outside_step"]["combine_backward"]
+    assert cb["avg_us"] > 0 and cb["avg_us_flushed"] > 0 and cb["bytes"] > 0
