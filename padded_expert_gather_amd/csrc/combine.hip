@@ -11,7 +11,8 @@
 //     step 6 of both pages; fp32 accumulation per their Ascend Guardrails).
 //
 //   combine backward: dy[row(a)] = w[a] * dout[a / K] in the expert layout
-//     (zero gap rows) and wgrad of dout, in one pass over dout.
+//     (zero gap rows) and wgrad of dout: in one pass over dout for K <= 2;
+//     for larger K a weighted gather of dout into dy, then the wgrad kernel.
 //
 // How: token-major. The token's rows (and weights) come in by wave-uniform
 // scalar loads, and each of the token's waves streams its slice of the H
@@ -682,8 +683,7 @@ static peg_status wgrad_launch(const void* y, const void* grad, int32_t dtype, i
     return wgrad_by_dtype<0>(dtype, vec, u, dim3((unsigned)tb), s, a);
 }
 
-// Waves per token of dy_gather_kernel: as the gather's (2 up to 512 row
-// vectors, else 4).
+// Arguments of the dy gather launch.
 struct DyArgs {
     const uint8_t* dout;
     uint8_t* dy;
@@ -738,7 +738,7 @@ static peg_status dy_gather(const void* dout, const float* weights, int32_t dtyp
     const int64_t nch = row_bytes / vec;
     const bool fill = dy_rows > 0 && use_gap_fill(layout, dy_rows, row_bytes, E);
     const int64_t nz = fill ? 0 : gap_blocks(dy_rows, nch);
-    const int wpt = nch <= 512 ? 2 : 4;
+    const int wpt = nch <= 512 ? 2 : 4;  // waves per token: the gather's for K > 2
     const int64_t tb = token_blocks(T, wpt);
     if (!grid_fits(tb + nz, kBlock)) return PEG_ERR_BAD_SHAPE;
     if (fill) PEG_CHECK(launch_gap_fill_vec(vec, (uint8_t*)dy, nch, dy_rows, E, capacity, bins, s));
