@@ -28,10 +28,15 @@
 
 namespace peg {
 
-#ifndef PEG_KBATCH
-#define PEG_KBATCH 4
+// The combine loads the vectors of up to PEG_COMBINE_INFLIGHT / U expert
+// rows (U vectors per lane each) before it uses them: 16 vectors per lane
+// in flight, 4 rows at 4 vectors per lane, 8 rows at 2 (T8192 H7168 K8,
+// 2 vectors per lane: 107.0 us at 8 rows against 110.4 at 4; T32768 H3584
+// K8, 4 vectors per lane: 155.7 us at 4 rows against 158.7 at 8 rows of 2
+// vectors).
+#ifndef PEG_COMBINE_INFLIGHT
+#define PEG_COMBINE_INFLIGHT 16
 #endif
-constexpr int kKBatch = PEG_KBATCH;  // expert rows loaded together before they are used
 #ifndef PEG_WGRAD_KBATCH
 #define PEG_WGRAD_KBATCH 2
 #endif
@@ -74,7 +79,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint8_t* __restri
     using L = Lanes<DT, VEC>;
     using V = typename L::V;
     constexpr int N = L::N;
-    constexpr int KB = KR < kKBatch ? KR : kKBatch;
+    constexpr int KBU = PEG_COMBINE_INFLIGHT / U > 0 ? PEG_COMBINE_INFLIGHT / U : 1;
+    constexpr int KB = KR < KBU ? KR : KBU;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t gw = xcd_block(blockIdx.x, gridDim.x) * (kBlock / kWave) + w;  // wave of the launch
     const int64_t t = gw / WPT;  // WPT 8 or 16: a token spans 2 or 4 blocks
