@@ -1,6 +1,8 @@
 """GPU: the entry points are capturable in a HIP graph (they allocate
 nothing, synchronise nothing and record no memset), and graph replays give
-the eager results.
+the eager results. The combine backward at K = 4 (its dy gather and wgrad
+launches, with a gap fill launch first for a binned dy of 128 MB) is captured
+and replayed on its own the same way.
 
 One step (route_prep -> gather -> combine -> wgrad -> combine backward) on
 preallocated buffers is captured once, then replayed three times with new
@@ -212,3 +214,61 @@ def test_graph_other_entry_points_match_eager():
                 g, e = g.view(torch.int16), e.view(torch.int16)
             assert torch.equal(g, e), (seed, k)
         assert int(got["flags"].item()) == 0
+
+
+@pytest.mark.parametrize("layout", [peg.PADDED, peg.BINNED])
+def test_graph_split_combine_backward(layout):
+    """The combine backward at K = 4 (a dy gather launch, then the wgrad
+    kernel; for the binned dy of 128 MB and more a gap fill launch first)
+    captured once and replayed three times with new upstream gradients and
+    weights written into the captured buffers: every replay equals the eager
+    call on the same inputs, bit for bit."""
+    Tb, Hb, Eb, Kb = 1024, 512, 8, 4
+    Cb = 16384 if layout == peg.BINNED else 0  # binned dy: 8 * 16384 rows * 1 KiB = 128 MiB
+    print(f"[graph split backward] layout{layout} T{Tb} H{Hb} E{Eb} K{Kb} C{Cb}", flush=True)
+    rng = np.random.default_rng(40 + layout)
+    top, _ = W.random_routing(rng, Tb, Kb, Eb, none_frac=0.05, skew=0.3)
+    top_d = to_dev(top)
+    r = peg.route_prep(top_d, Eb, capacity=Cb) if layout == peg.BINNED else peg.route_prep(top_d, Eb, pad_multiple=M)
+    R = Eb * Cb if layout == peg.BINNED else r.expert_rows()
+    y = to_dev(W.normal(rng, (R, Hb), W.BF16), W.BF16)
+    dout = torch.empty((Tb, Hb), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty(Tb * Kb, dtype=torch.float32, device=DEV)
+    dy = torch.empty((R, Hb), dtype=torch.bfloat16, device=DEV)
+    wg = torch.empty(Tb * Kb, dtype=torch.float32, device=DEV)
+    ws = torch.empty(peg.workspace_bytes(Tb, Kb, Eb), dtype=torch.uint8, device=DEV)
+    lib = peg.library()
+
+    def call():
+        st = torch.cuda.current_stream().cuda_stream
+        P = lambda t: None if t is None else t.data_ptr()
+        rc = lib.peg_combine_backward(P(y), P(dout), P(w), peg.BF16, layout, Tb, Hb, Kb, Eb, Cb, P(r.indices),
+                                      P(r.bin_ids), P(r.bins), P(r.padded_bins), P(r.slot_row), P(dy), R, P(wg),
+                                      P(ws), ws.numel(), st)
+        assert rc == 0
+
+    dout.copy_(to_dev(W.normal(rng, (Tb, Hb), W.BF16), W.BF16))
+    w.copy_(torch.from_numpy(rng.random(Tb * Kb, dtype=np.float32)).to(DEV))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dout.copy_(to_dev(W.normal(rng, (Tb, Hb), W.BF16), W.BF16))
+        w.copy_(torch.from_numpy(rng.random(Tb * Kb, dtype=np.float32)).to(DEV))
+        call()  # eager
+        torch.cuda.synchronize()
+        dy_e, wg_e = dy.clone(), wg.clone()
+        dy.fill_(7.0)
+        wg.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dy.view(torch.int16), dy_e.view(torch.int16)), f"replay {rep}: dy differs from eager"
+        assert torch.equal(wg, wg_e), f"replay {rep}: wgrad differs from eager"
