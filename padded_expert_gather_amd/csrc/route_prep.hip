@@ -322,8 +322,12 @@ __global__ __launch_bounds__(kScanThreads) void tile_scan_kernel(int32_t* __rest
 // bins and padded_bins.
 // SB: table loads each placement thread keeps in flight while summing the
 // table (1, 4 or 32: about the tiles one thread sums; 64 at once measured
-// 16.2 against 14.4 us at T8192 K8 E256).
-template <int ITEMS, int SB>
+// 16.2 against 14.4 us at T8192 K8 E256). V4: E is a multiple of 4 and a
+// thread reads 4 consecutive experts of a tile row in one 16-byte load
+// (SB of them in flight: 1, 4 or 16), so that a thread sums a quarter of
+// the tiles it would otherwise; at T32768 K8 E64 and T8192 K8 E256 a thread
+// then sums 16 tiles in one round of loads instead of 64 in two.
+template <int ITEMS, int SB, bool V4>
 __global__ __launch_bounds__(kBlock) void tile_place_kernel(
     const int32_t* __restrict__ top, int64_t total, int32_t E, int32_t nbits, const int32_t* __restrict__ counts,
     int64_t ntiles, int32_t bases_ready, int32_t pad_multiple, int32_t layout, int32_t capacity,
@@ -366,7 +370,47 @@ __global__ __launch_bounds__(kBlock) void tile_place_kernel(
             pstart[e] = 0;
         }
         lds_barrier();
-        {
+        if constexpr (V4) {
+            // threads in groups of min(E / 4, kBlock): thread j of group g
+            // sums experts 4j .. 4j+3 over the tiles g, g + groups, ...
+            const int E4 = E / 4;
+            const int eslots = E4 <= kBlock ? E4 : kBlock;
+            const int groups = kBlock / eslots;
+            const int g = threadIdx.x / eslots;
+            const int4* rows4 = reinterpret_cast<const int4*>(counts);
+            if (g < groups) {
+                for (int j = threadIdx.x - g * eslots; j < E4; j += eslots) {
+                    int run[4] = {0, 0, 0, 0}, run_before[4] = {0, 0, 0, 0};
+                    for (int64_t t0 = g; t0 < ntiles; t0 += (int64_t)groups * SB) {
+                        int4 cb[SB];
+#pragma unroll
+                        for (int q = 0; q < SB; ++q) {
+                            const int64_t t = t0 + (int64_t)q * groups;
+                            cb[q] = t < ntiles ? rows4[t * E4 + j] : make_int4(0, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int q = 0; q < SB; ++q) {
+                            const bool before = t0 + (int64_t)q * groups < (int64_t)blockIdx.x;
+                            run[0] += cb[q].x;
+                            run[1] += cb[q].y;
+                            run[2] += cb[q].z;
+                            run[3] += cb[q].w;
+                            if (before) {
+                                run_before[0] += cb[q].x;
+                                run_before[1] += cb[q].y;
+                                run_before[2] += cb[q].z;
+                                run_before[3] += cb[q].w;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (run[i]) atomicAdd(&pstart[4 * j + i], run[i]);
+                        if (run_before[i]) atomicAdd(&tbase[4 * j + i], run_before[i]);
+                    }
+                }
+            }
+        } else {
             // threads in groups of min(E, kBlock): thread e of group g sums
             // expert e over the tiles g, g + groups, ... (SB loads in flight
             // at a time; each load instruction of a wave reads consecutive
@@ -465,6 +509,9 @@ static int id_bits(int E) {
 #define PEG_MERGED_MAX_TABLE 16384
 #endif
 constexpr int64_t kMergedMaxTable = PEG_MERGED_MAX_TABLE;
+#ifndef PEG_PLACE_V4
+#define PEG_PLACE_V4 1
+#endif
 
 template <int ITEMS>
 static peg_status place_tiles(const int32_t* top, int64_t total, int32_t E, int32_t layout, int32_t capacity,
@@ -477,15 +524,27 @@ static peg_status place_tiles(const int32_t* top, int64_t total, int32_t E, int3
                          bins, padded_bins));
     if (ntiles == 0) return PEG_OK;
     const size_t lds = ((size_t)(kBlock / kWave) * E + 3 * (size_t)E) * sizeof(int);
+#define PEG_PLACE_LAUNCH(SB, V4)                                                                                \
+    return launch(tile_place_kernel<ITEMS, SB, V4>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total,   \
+                  E, id_bits(E), counts, ntiles, merged ? 0 : 1, pad_multiple, layout, capacity, indices, bin_ids,  \
+                  tpe, bins, padded_bins, slot_row)
     const int64_t groups = kBlock / (E <= kBlock ? E : kBlock);
     const int64_t per = merged ? (ntiles + groups - 1) / groups : 1;  // tiles one thread sums
-#define PEG_PLACE_LAUNCH(SB)                                                                                    \
-    return launch(tile_place_kernel<ITEMS, SB>, dim3((unsigned)ntiles), dim3(kBlock), lds, s, top, total, E,    \
-                  id_bits(E), counts, ntiles, merged ? 0 : 1, pad_multiple, layout, capacity, indices, bin_ids, tpe, \
-                  bins, padded_bins, slot_row)
-    if (per <= 1) PEG_PLACE_LAUNCH(1);
-    if (per <= 4) PEG_PLACE_LAUNCH(4);
-    PEG_PLACE_LAUNCH(32);
+    // 16-byte table loads when a thread would sum more than 4 tiles and every
+    // tile row starts 16-byte aligned (T32768 K8 E64: route_prep 14.3 ->
+    // 12.9 us, T8192 K8 E256: 14.5 -> 12.6; with E = 8, 1-2 tiles per
+    // thread, the 4-byte loads stay: 8.5 against 9.2 us for the fused gating
+    // at T16384 K2)
+    if (per > 4 && PEG_PLACE_V4 && E % 4 == 0 && (reinterpret_cast<uintptr_t>(counts) & 15) == 0) {
+        const int64_t groups4 = kBlock / (E / 4 <= kBlock ? E / 4 : kBlock);
+        const int64_t per4 = (ntiles + groups4 - 1) / groups4;
+        if (per4 <= 1) PEG_PLACE_LAUNCH(1, true);
+        if (per4 <= 4) PEG_PLACE_LAUNCH(4, true);
+        PEG_PLACE_LAUNCH(16, true);
+    }
+    if (per <= 1) PEG_PLACE_LAUNCH(1, false);
+    if (per <= 4) PEG_PLACE_LAUNCH(4, false);
+    PEG_PLACE_LAUNCH(32, false);
 #undef PEG_PLACE_LAUNCH
 }
 
