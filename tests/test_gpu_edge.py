@@ -363,14 +363,16 @@ def test_combine_backward_rows_past_layout(layout, K):
     assert bool((buf[R + extra:] == -7.0).all()), "a row past dy_rows was written"
 
 
+@pytest.mark.parametrize("empty", [False, True])
 @pytest.mark.parametrize("K", [2, 4])
 @pytest.mark.parametrize("layout", [W.BINNED, W.PADDED])
-def test_combine_backward_short_dy(layout, K):
-    """dy with fewer rows than the layout's R: rows [0, dy_rows) as the
-    oracle's (kept rows w * dout, gaps zero), nothing written at or past
-    dy_rows, and wgrad still computed for the routes whose rows lie there
-    (equal, bit for bit, to the wgrad kernel's)."""
-    print(f"[backward short dy] layout{layout} K{K}", flush=True)
+def test_combine_backward_short_dy(layout, K, empty):
+    """dy with fewer rows than the layout's R (about half of them, or none):
+    rows [0, dy_rows) as the oracle's (kept rows w * dout, gaps zero),
+    nothing written at or past dy_rows, and wgrad still computed for the
+    routes whose rows lie there (equal, bit for bit, to the wgrad
+    kernel's)."""
+    print(f"[backward short dy] layout{layout} K{K} empty{empty}", flush=True)
     rng = np.random.default_rng(40 + layout + 7 * K)
     T, E, H, C, m = 200, 5, 136, 30 * K, 8
     top, w = W.random_routing(rng, T, K, E, skew=0.3, none_frac=0.1)
@@ -380,8 +382,8 @@ def test_combine_backward_short_dy(layout, K):
     rg = peg.route_prep(to_dev(top), E, capacity=cap, pad_multiple=None if cap else m)
     R = oracle.expert_rows(ro, layout, cap)
     rows = oracle.assignment_rows(ro, layout, cap)
-    short = R // 2 + 3
-    assert 0 < short < R and (rows >= short).any()
+    short = 0 if empty else R // 2 + 3
+    assert 0 <= short < R and (rows >= short).any()
     yr = W.expert_tensor_rows(rng, R, H, W.BF16, used_rows=rows[rows >= 0])
     yrg, gg, wg = to_dev(yr, W.BF16), to_dev(grad, W.BF16), to_dev(w.reshape(-1))
     buf = torch.full((R, H), -7.0, dtype=torch.bfloat16, device=DEV)
