@@ -208,7 +208,8 @@ peg_status peg_gather_padded(const void* x, int32_t dtype, int64_t T, int64_t H,
 /*
  * peg_scatter_combine - inverse of the gathers: weighted top-k combine.
  * [BIN] Workflow step 5; [PAD] Workflow step 6 and Ascend Guardrails (weights
- * indexed by assignment id); [FMD] "unpermute + weighted combine".
+ * indexed by assignment id); [FMD] pipeline diagram, its final stage (undo
+ * the permutation, combine with the gating weights).
  *
  * out[t, :] = sum over k = 0..K-1 (ascending) with assignment a = t*K + k
  * kept, of w[a] * y[row(a), :], accumulated in fp32 and rounded once to the

@@ -16,7 +16,9 @@
  *
  * Parity status per function is stated in the function comments; each is
  * pinned by the CPU tests against brute force, library routines, closed
- * forms and the pages' invariants.
+ * forms and the pages' invariants. One case is parity unpinned: a routing
+ * map row with more than topk routes (pego_routing_map_compact), where no
+ * page fixes which routes are kept.
  */
 #include "peg_oracle.h"
 
@@ -232,7 +234,7 @@ static int64_t valid_count(const int32_t* bins, int32_t E, int64_t total) {
 
 /*
  * Row of every assignment id ([BIN] Workflow step 5 / [PAD] step 6: the
- * scatter goes back "through unique assignment ids"): rows_out[a] is the
+ * scatter is indexed by assignment id, each id unique): rows_out[a] is the
  * expert-tensor row holding assignment a, -1 if a has no route or was
  * dropped by the capacity limit.
  */
@@ -543,8 +545,11 @@ int pego_combine_backward_dy(const void* dout, int32_t dtype, int64_t T, int64_t
  * increasing expert index; routed experts fill the output slots in that
  * order, at most topk of them; the rest of the row is padded with index -1
  * and probability 0. Probabilities are returned as float32.
- * A row with more than topk routes keeps its topk lowest expert ids (the
- * reading taken of "maximum number of valid routes emitted per token").
+ * A row with more than topk routes keeps its topk lowest expert ids: the
+ * page gives topk as the most routes a token emits and does not say which
+ * ones survive; this is the reading taken. Parity unpinned for such rows:
+ * no page value fixes the choice (the pins check it against the same
+ * reading written as a plain row walk).
  */
 int pego_routing_map_compact(const void* probs, int32_t probs_dtype, const uint8_t* routing_map,
                              int64_t T, int32_t E, int32_t topk, float* probs_out,
