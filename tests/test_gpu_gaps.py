@@ -11,8 +11,8 @@ large multiple; padded with a multiple of 2 and a buffer far longer than the
 padded rows, so that each gap block's range crosses the gaps of many
 experts (rows past padded_bins[E-1] must stay untouched); a buffer cut short
 of padded_bins[E-1]; E = 1 and E = 64; all routes absent. Plus float16
-through the K = 8 gather, combine, wgrad and combine backward over a binned
-tensor of 128 MiB, against the oracle on every element.
+and float32 through the K = 8 gather, combine, wgrad and combine backward
+over a binned tensor of 128 / 256 MiB, against the oracle on every element.
 """
 import numpy as np
 import pytest
@@ -215,40 +215,41 @@ def test_large_binned_dy_rows_past_layout(K):
     assert torch.equal(wgb, peg.wgrad(y, dg, rg)), "fused wgrad == wgrad kernel"
 
 
-def test_large_f16_binned_k8_against_oracle():
-    """Float16 through the K = 8 paths over a binned tensor of 128 MiB (its
-    gap rows from the fill-shaped launch): the gather bit for bit, the
-    combine and wgrad on an independent NaN-sentinel y, and the combine
-    backward (its dy gather with float16 scaling, then the wgrad kernel)
-    against the oracle on every element; the backward's wgrad equals the
-    wgrad kernel's bit for bit."""
+@pytest.mark.parametrize("dtype", [W.F16, W.F32])
+def test_large_binned_k8_against_oracle(dtype):
+    """Float16 and float32 through the K = 8 paths over a binned tensor of
+    128 / 256 MiB (its gap rows from the fill-shaped launch): the gather bit
+    for bit, the combine and wgrad on an independent NaN-sentinel y, and the
+    combine backward (its dy gather with scaling in the element type, then
+    the wgrad kernel) against the oracle on every element; the backward's
+    wgrad equals the wgrad kernel's bit for bit."""
     from gpu_util import assert_close
-    print("[gaps f16 K8]", flush=True)
-    rng = np.random.default_rng(51)
+    print(f"[gaps K8 dtype{dtype}]", flush=True)
+    rng = np.random.default_rng(51 + dtype)
     T, K, E, H, C = 8192, 8, 16, 1024, 4096
-    assert E * C * H * 2 >= 128 << 20
+    assert E * C * H * ELEM[dtype] >= 128 << 20
     top, w = W.random_routing(rng, T, K, E, none_frac=0.05, skew=0.15)
-    x = W.normal(rng, (T, H), W.F16)
-    grad = W.normal(rng, (T, H), W.F16)
+    x = W.normal(rng, (T, H), dtype)
+    grad = W.normal(rng, (T, H), dtype)
     ro = oracle.route_prep(top, E)
     rg = peg.route_prep(to_dev(top), E, capacity=C)
     rows = oracle.assignment_rows(ro, W.BINNED, C)
     bits_equal(to_host(rg.slot_row), rows, "slot_row")
     # gather into a 0xFF-filled buffer: every row written
-    buf = _filled(E * C, H, W.F16)
-    peg.gather_binned(to_dev(x, W.F16), rg, out=buf)
+    buf = _filled(E * C, H, dtype)
+    peg.gather_binned(to_dev(x, dtype), rg, out=buf)
     bits_equal(to_host(buf), oracle.gather(x, ro, W.BINNED, C), "gather")
     del buf
     # combine and wgrad on an independent y whose unused rows are NaN
-    yr = W.expert_tensor_rows(rng, E * C, H, W.F16, used_rows=rows[rows >= 0])
-    yg, gg, wg = to_dev(yr, W.F16), to_dev(grad, W.F16), to_dev(w.reshape(-1))
-    so, S = oracle.scatter_combine(yr, W.F16, ro, W.BINNED, C, weights=w.reshape(-1), with_scale=True)
-    assert_close(to_host(peg.scatter_combine(yg, rg, weights=wg)), so, S, W.F16, "combine")
-    wo, WS = oracle.wgrad(yr, grad, W.F16, ro, W.BINNED, C, with_scale=True)
+    yr = W.expert_tensor_rows(rng, E * C, H, dtype, used_rows=rows[rows >= 0])
+    yg, gg, wg = to_dev(yr, dtype), to_dev(grad, dtype), to_dev(w.reshape(-1))
+    so, S = oracle.scatter_combine(yr, dtype, ro, W.BINNED, C, weights=w.reshape(-1), with_scale=True)
+    assert_close(to_host(peg.scatter_combine(yg, rg, weights=wg)), so, S, dtype, "combine")
+    wo, WS = oracle.wgrad(yr, grad, dtype, ro, W.BINNED, C, with_scale=True)
     wk = peg.wgrad(yg, gg, rg)
     assert_close(to_host(wk), wo, WS, W.F32, "wgrad")
     # combine backward (K = 8: dy gather, then the wgrad kernel)
-    dyo = oracle.combine_backward_dy(grad, W.F16, ro, W.BINNED, C, weights=w.reshape(-1))
+    dyo = oracle.combine_backward_dy(grad, dtype, ro, W.BINNED, C, weights=w.reshape(-1))
     dyg, wgb = peg.combine_backward(yg, gg, rg, weights=wg, dy_rows=E * C)
-    assert_close(to_host(dyg), dyo, np.abs(W.to_f32(dyo, W.F16).astype(np.float64)), W.F16, "backward dy")
+    assert_close(to_host(dyg), dyo, np.abs(W.to_f32(dyo, dtype).astype(np.float64)), dtype, "backward dy")
     assert torch.equal(wgb, wk), "backward wgrad == wgrad kernel"
