@@ -827,6 +827,8 @@ PEG_API peg_status peg_combine_backward(const void* y, const void* dout, const f
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     PEG_CHECK(ensure_slots(T, K, E, layout, capacity, indices, bin_ids, bins, padded_bins, &slot_row, ws, ws_bytes, s));
     if (K > PEG_BACKWARD_SPLIT_K) {
+        // both launches' sizes checked before the first is queued
+        if (!grid_fits(token_blocks(T, wgrad_shape(K, H * eb / vec).wpt), kBlock)) return PEG_ERR_BAD_SHAPE;
         PEG_CHECK(dy_gather(dout, weights, dtype, vec, layout, T, H, K, E, capacity, bins, padded_bins, slot_row, dy,
                             dy_rows, s));
         return wgrad_launch(y, dout, dtype, vec, layout, T, H, K, E, capacity, bins, padded_bins, slot_row, wgrad,

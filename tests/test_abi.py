@@ -266,6 +266,10 @@ def test_oversized_launches_refused(lib):
     w = lib.peg_wgrad
     assert w(_p(FAKE), _p(FAKE), 1, 0, 80_000_000, 8, 2, 4, 2, _p(FAKE), _p(FAKE), _p(FAKE), None, _p(FAKE),
              _p(FAKE), _p(FAKE), 1 << 20, None) == BAD_SHAPE
+    cb = lib.peg_combine_backward  # K = 2 (one pass) and K = 4 (dy gather, then wgrad)
+    for K in (2, 4):
+        assert cb(_p(FAKE), _p(FAKE), None, 1, 0, 80_000_000 // K * 2, 8, K, 4, 2, _p(FAKE), _p(FAKE), _p(FAKE),
+                  None, _p(FAKE), _p(FAKE), 8, _p(FAKE), _p(FAKE), 1 << 20, None) == BAD_SHAPE, K
     r = lib.peg_router_topk
     assert r(_p(FAKE), 0, 1 << 29, 2, 1, 0, 1, _p(FAKE), _p(FAKE), None) == BAD_SHAPE
     f = lib.peg_routing_map_compact
