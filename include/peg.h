@@ -69,7 +69,8 @@ typedef int32_t peg_status;
 /* Limits enforced by the host checks. Besides the limits each call lists,
  * every call returns PEG_ERR_BAD_SHAPE when one of its launches would exceed
  * 2^32 - 1 threads (a HIP dispatch counts its threads in 32 bits), before
- * any of its launches is queued: for the row kernels (2 to 8 waves of 64
+ * it writes any output (a call given slot_row = NULL may have rebuilt the row
+ * map into its workspace by then): for the row kernels (2 to 8 waves of 64
  * per token, 4 waves per block) this is T above about 33.5 million tokens
  * at 2 waves per token down to 8.4 million at 8. */
 #define PEG_MAX_EXPERTS 1024
