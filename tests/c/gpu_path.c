@@ -10,7 +10,10 @@
  * Index outputs and the gathered tensor must match bit for bit; the combine
  * and wgrad must be within |gpu - oracle| <= rtol*|oracle| + 1e-5*scale,
  * rtol 2e-2 for the bf16 combine and 1e-5 for the float wgrad, where scale
- * is the oracle's sum of the magnitudes of the terms.
+ * is the oracle's sum of the magnitudes of the terms. The combine backward
+ * (dout = the gradient rows; one pass at K = 2, the dy gather then the
+ * wgrad kernel at K = 4): dy within one bf16 rounding of the oracle's, its
+ * wgrad equal to the wgrad kernel's bit for bit.
  *
  * Exit status 0 and a last line "gpu_path ok" when every check passes.
  */
@@ -166,6 +169,12 @@ static void run_case(const char* tag, int64_t T, int64_t H, int32_t K, int32_t E
                                 d_w, d_out, ws, ws_bytes, NULL));
     PEG_OK_(peg_wgrad(d_y, d_grad, PEG_BF16, layout, T, H, K, E, capacity, d_idx, d_bid, d_bins, d_pbins, d_slot,
                       d_wg, ws, ws_bytes, NULL));
+    /* the combine backward with dout = grad: one pass for K <= 2, the dy
+       gather then the wgrad kernel for larger K */
+    void* d_dy = dev_copy(NULL, 2 * (size_t)(R * H));
+    float* d_wgb = dev_copy(NULL, sizeof(float) * n_ids);
+    PEG_OK_(peg_combine_backward(d_y, d_grad, d_w, PEG_BF16, layout, T, H, K, E, capacity, d_idx, d_bid, d_bins,
+                                 d_pbins, d_slot, d_dy, R, d_wgb, ws, ws_bytes, NULL));
     HIP_OK(hipDeviceSynchronize());
 
     int32_t* g_idx = host_copy(d_idx, sizeof(int32_t) * n_ids);
@@ -176,6 +185,8 @@ static void run_case(const char* tag, int64_t T, int64_t H, int32_t K, int32_t E
     uint16_t* g_y = host_copy(d_y, 2 * (size_t)(R * H));
     uint16_t* g_out = host_copy(d_out, 2 * (size_t)(T * H));
     float* g_wg = host_copy(d_wg, sizeof(float) * n_ids);
+    uint16_t* g_dy = host_copy(d_dy, 2 * (size_t)(R * H));
+    float* g_wgb = host_copy(d_wgb, sizeof(float) * n_ids);
 
     /* oracle on the same inputs */
     int32_t* o_idx = malloc(sizeof(int32_t) * at_least1(n_ids));
@@ -199,6 +210,12 @@ static void run_case(const char* tag, int64_t T, int64_t H, int32_t K, int32_t E
                          NULL, 0, o_out, o_out_scale);
     pego_wgrad(o_y, grad, PEGO_BF16, R, T, H, K, E, layout, capacity, o_idx, o_bid, o_bins, o_pbins, NULL, 0, o_wg,
                o_wg_scale);
+    uint16_t* o_dy = calloc(at_least1(R * H), 2);
+    if (pego_combine_backward_dy(grad, PEGO_BF16, T, H, K, E, layout, capacity, o_idx, o_bid, o_bins, o_pbins,
+                                 weights, R, NULL, 0, o_dy) != 0) {
+        fprintf(stderr, "FAIL %s: oracle refused the backward\n", tag);
+        exit(4);
+    }
 
     expect_bytes(g_idx, o_idx, sizeof(int32_t) * n_ids, "indices", tag);
     expect_bytes(g_bid, o_bid, sizeof(int32_t) * n_ids, "bin_ids", tag);
@@ -222,15 +239,21 @@ static void run_case(const char* tag, int64_t T, int64_t H, int32_t K, int32_t E
                      "combine", tag, i);
     for (int64_t i = 0; i < n_ids; ++i)
         expect_close(g_wg[i], o_wg[i], o_wg_scale[i], 1e-5, "wgrad", tag, i);
+    for (int64_t i = 0; i < R * H; ++i) {  /* one rounding of a product: S = |oracle| */
+        const double o = pego_load(o_dy, PEGO_BF16, i);
+        expect_close(pego_load(g_dy, PEGO_BF16, i), o, fabs(o), 2e-2, "combine backward dy", tag, i);
+    }
+    expect_bytes(g_wgb, g_wg, sizeof(float) * n_ids, "combine backward wgrad (== the wgrad kernel's)", tag);
     printf("%s: T%lld H%lld K%d E%d R%lld checked\n", tag, (long long)T, (long long)H, K, E, (long long)R);
     fflush(stdout);
 
     void* dev_bufs[] = {ws, d_top, d_w, d_x, d_grad, d_idx, d_bid, d_tpe, d_bins, d_pbins, d_slot, d_y, d_err,
-                        d_out, d_wg};
+                        d_out, d_wg, d_dy, d_wgb};
     for (size_t i = 0; i < sizeof(dev_bufs) / sizeof(dev_bufs[0]); ++i)
         if (dev_bufs[i]) HIP_OK(hipFree(dev_bufs[i]));
-    void* host_bufs[] = {top, weights, x, grad, g_idx, g_bid, g_tpe, g_bins, g_slot, g_y, g_out, g_wg, o_idx,
-                         o_bid, o_tpe, o_bins, o_pbins, o_slot, o_y, o_out, o_out_scale, o_wg, o_wg_scale};
+    void* host_bufs[] = {top, weights, x, grad, g_idx, g_bid, g_tpe, g_bins, g_slot, g_y, g_out, g_wg, g_dy, g_wgb,
+                         o_idx, o_bid, o_tpe, o_bins, o_pbins, o_slot, o_y, o_out, o_out_scale, o_wg, o_wg_scale,
+                         o_dy};
     for (size_t i = 0; i < sizeof(host_bufs) / sizeof(host_bufs[0]); ++i) free(host_bufs[i]);
 }
 
