@@ -498,8 +498,8 @@ static RowShape combine_shape(int32_t K, int64_t nch) {
 }
 // K > 2 with rows above PEG_WGRAD_SPLIT vectors: PEG_WGRAD_WPT_LONG waves
 // per token (T8192 H7168 K8: wgrad 90.5 us at 4 waves against 94.9 at 2,
-// the combine backward 271.6 against 283.7; T32768 H3584 K8 keeps 2: wgrad
-// 121.5 us against 131.5 at 4).
+// the one-pass combine backward 271.6 against 283.7; T32768 H3584 K8 keeps
+// 2: wgrad 121.5 us against 131.5 at 4).
 #ifndef PEG_WGRAD_SPLIT
 #define PEG_WGRAD_SPLIT 512
 #endif
@@ -526,7 +526,8 @@ static RowShape wgrad_shape(int32_t K, int64_t nch) {
 #ifndef PEG_BACKWARD_WPT
 #define PEG_BACKWARD_WPT PEG_WGRAD_WPT
 #endif
-// The combine backward with K > 2 keeps 4 vectors per lane per pass
+// The one-pass combine backward with K > 2 (which runs only when
+// PEG_BACKWARD_SPLIT_K is raised above 2) keeps 4 vectors per lane per pass
 // (T8192 H7168 K8: 250.8 us against 262.2 at 2; T32768 H3584 K8 509.9
 // against 511.1).
 #ifndef PEG_BACKWARD_UMAX
