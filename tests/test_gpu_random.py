@@ -8,8 +8,11 @@ integer outputs and gathers bit for bit, floating outputs within the
 tolerance of tests/gpu_util.py. A second set of seeds draws shapes for the
 compaction and its backward, the router gating alone and fused with
 route_prep, and row windows. The seed is in the test id, so a failure names
-its case.
+its case. PEG_RANDOM_SEEDS=N in the environment runs N seeds of each set
+(default 150 and 60).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -21,7 +24,10 @@ from test_gpu_edge import check_combine_backward
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(150))
+# seeds of the two sets (150 and 60); PEG_RANDOM_SEEDS=N runs N of each
+_N = os.environ.get("PEG_RANDOM_SEEDS")
+SEEDS = list(range(int(_N) if _N else 150))
+OTHER_SEEDS = list(range(int(_N) if _N else 60))
 
 
 def _draw(seed):
@@ -84,7 +90,7 @@ def _draw_aux(seed):
     return rng, T, K, E
 
 
-@pytest.mark.parametrize("seed", list(range(60)))
+@pytest.mark.parametrize("seed", OTHER_SEEDS)
 def test_random_compaction_router_windows(seed):
     """Compaction (and its backward), router gating alone and fused with
     route_prep, and routing into row windows, at one random shape each."""
